@@ -1,0 +1,160 @@
+"""ctypes front end of the CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the product package.  Arrays are numpy:
+bf16 data as uint16 bit patterns, indices as int32, results as float64.
+
+`Oracle(path)` binds one build of oracle.c (tests load deliberately mutated
+builds through it); the module-level functions use the default build.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+
+def _u16(a):
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, a.dtype
+    return a
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what}: inputs outside what the tables cover (rc={rc})")
+
+
+class Oracle:
+    def __init__(self, path):
+        lib = ctypes.CDLL(path)
+        P, I, Dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_double
+        lib.oracle_kv_append.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I]
+        lib.oracle_decode.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, Dbl]
+        lib.oracle_decode_online.argtypes = lib.oracle_decode.argtypes
+        lib.oracle_prefill_causal.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I,
+                                              I, I, Dbl, P, I]
+        lib.oracle_decode_partials.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I,
+                                               I, I, I, Dbl, I, I]
+        lib.oracle_lse_merge.argtypes = [P, P, P, P, I, I, I]
+        for f in (lib.oracle_kv_append, lib.oracle_decode, lib.oracle_decode_online,
+                  lib.oracle_prefill_causal, lib.oracle_decode_partials,
+                  lib.oracle_lse_merge):
+            f.restype = ctypes.c_int
+        self.lib = lib
+        self.path = path
+
+    def kv_append(self, k_cache, v_cache, k_new, v_new, block_tables, context_lens,
+                  cu_new_lens=None):
+        """In place on the numpy uint16 pools k_cache/v_cache [N][Hkv][bs][D]."""
+        assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+        assert k_cache.dtype == np.uint16 and v_cache.dtype == np.uint16
+        N, Hkv, bs, D = k_cache.shape
+        bt, cl = _i32(block_tables), _i32(context_lens)
+        cu = None if cu_new_lens is None else _i32(cu_new_lens)
+        kn, vn = _u16(k_new), _u16(v_new)
+        rc = self.lib.oracle_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(kn), _ptr(vn),
+                                       _ptr(bt), _ptr(cl), _ptr(cu), bt.shape[0], Hkv, D,
+                                       bs, bt.shape[1], N)
+        _check(rc, "kv_append")
+
+    def decode(self, q, k_cache, v_cache, block_tables, context_lens, scale,
+               online=False):
+        """q [B][Hq][D] uint16 -> out [B][Hq][D] float64."""
+        q, k_cache, v_cache = _u16(q), _u16(k_cache), _u16(v_cache)
+        B, Hq, D = q.shape
+        N, Hkv, bs, _ = k_cache.shape
+        bt, cl = _i32(block_tables), _i32(context_lens)
+        out = np.zeros((B, Hq, D), dtype=np.float64)
+        fn = self.lib.oracle_decode_online if online else self.lib.oracle_decode
+        rc = fn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
+                B, Hq, Hkv, D, bs, bt.shape[1], N, float(scale))
+        _check(rc, "decode")
+        return out
+
+    def prefill_causal(self, q, k_cache, v_cache, block_tables, context_lens, cu_q_lens,
+                       scale, rows=None):
+        """q [T][Hq][D] uint16 -> out [T][Hq][D] float64 (unlisted rows stay NaN)."""
+        q, k_cache, v_cache = _u16(q), _u16(k_cache), _u16(v_cache)
+        T, Hq, D = q.shape
+        N, Hkv, bs, _ = k_cache.shape
+        bt, cl, cu = _i32(block_tables), _i32(context_lens), _i32(cu_q_lens)
+        out = np.full((T, Hq, D), np.nan, dtype=np.float64)
+        r = None if rows is None else _i32(rows)
+        rc = self.lib.oracle_prefill_causal(
+            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
+            _ptr(cu), bt.shape[0], Hq, Hkv, D, bs, bt.shape[1], N, float(scale),
+            _ptr(r), 0 if r is None else len(r))
+        _check(rc, "prefill_causal")
+        return out
+
+    def decode_partials(self, q, k_cache, v_cache, block_tables, context_lens, scale,
+                        partition_size):
+        """Per-partition (o, m, l) of the split-context formulation."""
+        q, k_cache, v_cache = _u16(q), _u16(k_cache), _u16(v_cache)
+        B, Hq, D = q.shape
+        N, Hkv, bs, _ = k_cache.shape
+        bt, cl = _i32(block_tables), _i32(context_lens)
+        P = max(1, -(-int(cl.max(initial=0)) // partition_size))
+        o = np.zeros((B, Hq, P, D))
+        m = np.zeros((B, Hq, P))
+        l = np.zeros((B, Hq, P))
+        rc = self.lib.oracle_decode_partials(
+            _ptr(o), _ptr(m), _ptr(l), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt),
+            _ptr(cl), B, Hq, Hkv, D, bs, bt.shape[1], N, float(scale), partition_size, P)
+        _check(rc, "decode_partials")
+        return o, m, l
+
+    def lse_merge(self, o, m, l):
+        """Merge partials o [..][P][D], m/l [..][P] -> [..][D]."""
+        lead = o.shape[:-2]
+        P, D = o.shape[-2:]
+        o2 = np.ascontiguousarray(o, dtype=np.float64).reshape(-1, P, D)
+        m2 = np.ascontiguousarray(m, dtype=np.float64).reshape(-1, P)
+        l2 = np.ascontiguousarray(l, dtype=np.float64).reshape(-1, P)
+        out = np.zeros((o2.shape[0], D))
+        rc = self.lib.oracle_lse_merge(_ptr(out), _ptr(o2), _ptr(m2), _ptr(l2),
+                                       o2.shape[0], P, D)
+        _check(rc, "lse_merge")
+        return out.reshape(*lead, D)
+
+
+_default = None
+
+
+def default() -> Oracle:
+    global _default
+    if _default is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        _default = Oracle(_build.LIB)
+    return _default
+
+
+def kv_append(*a, **k):
+    return default().kv_append(*a, **k)
+
+
+def decode(*a, **k):
+    return default().decode(*a, **k)
+
+
+def prefill_causal(*a, **k):
+    return default().prefill_causal(*a, **k)
+
+
+def decode_partials(*a, **k):
+    return default().decode_partials(*a, **k)
+
+
+def lse_merge(*a, **k):
+    return default().lse_merge(*a, **k)
