@@ -1,0 +1,177 @@
+/*
+ * pagedkv.h -- C ABI of the MI355X (gfx950) paged KV-cache attention library
+ * (libpagedkv.so).
+ *
+ * The operations are those the tiny-vLLM pages name for the attention part of
+ * an inference engine: a KV cache kept in fixed-size pages ("blocks") that a
+ * per-sequence block table maps from logical to physical blocks, attention
+ * with grouped-query heads, a FlashAttention-style online softmax, decode (one
+ * new query token per sequence) and causal prefill (a whole prompt).
+ *   - paper-digest page "Tiny-vLLM: a high-performance LLM inference engine in
+ *     C++ and CUDA", section "Core Mechanics" (KV cache, online softmax,
+ *     PagedAttention, GQA, causal mask);
+ *   - tiny-vllm README (Korean translation), feature list and table of
+ *     contents ("Prefill vs decode", "Why KV cache exists", "Attention",
+ *     "GQA", "Softmax", "Causal mask", "Online softmax", "Paged Attention",
+ *     "Paged KV cache", "Paged Attention CUDA kernel");
+ *   - nano-vLLM guide announcement, ch. 3 "KV Cache", ch. 4 "PagedAttention",
+ *     ch. 6 "Prefill vs Decode".
+ *
+ * Conventions for every entry point
+ *   - All array arguments are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees or keeps them.  `stream` is a
+ *     hipStream_t passed as void* (NULL = the default stream).
+ *   - Work is enqueued asynchronously on `stream`; the return value reports
+ *     argument validation and the launch itself (hipGetLastError), not the
+ *     completion of the kernels.
+ *   - bf16 means IEEE bfloat16 bit patterns (uint16).  Indices are int32.
+ *   - Pool layout (both K and V, one pool per layer):
+ *         cache[num_blocks][Hkv][block_size][D]
+ *     so one (block, KV head) is block_size*D*2 bytes contiguous and one
+ *     token's D-vector is a 2*D = 128-byte row at D = 64.
+ *   - Query head h reads KV head h / (Hq / Hkv).
+ *   - context_lens[b] is the number of valid tokens of sequence b AFTER this
+ *     step's append.  Logical token j of sequence b is row j % block_size of
+ *     physical block block_tables[b * max_blocks_per_seq + j / block_size].
+ *   - Table entries past ceil(context_lens[b] / block_size) and pool rows past
+ *     the context are never read.  Physical ids outside [0, num_blocks) and
+ *     contexts longer than max_blocks_per_seq * block_size are data errors:
+ *     the kernels never touch memory outside the pools for them (such blocks
+ *     are skipped) but the result for that sequence is then undefined.
+ *   - Return: PKV_OK, or a negative status; pagedkv_last_error() gives text.
+ *     Validation happens on the host before any HIP call, so invalid
+ *     arguments never reach the device.  B == 0 (or no new tokens) returns
+ *     PKV_OK without launching anything.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Symbols of the C ABI are the only ones the shared library exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define PKV_API __attribute__((visibility("default")))
+#else
+#define PKV_API
+#endif
+
+#define PKV_OK 0
+#define PKV_ERR_INVALID_ARG (-1) /* null pointer, negative or inconsistent size */
+#define PKV_ERR_UNSUPPORTED (-2) /* shape this build does not implement         */
+#define PKV_ERR_WORKSPACE (-3)   /* workspace missing or too small              */
+#define PKV_ERR_HIP (-4)         /* a HIP runtime call or kernel launch failed  */
+
+#define PKV_OUT_BF16 0 /* output written as bf16, round to nearest even */
+#define PKV_OUT_F32 1  /* output written as fp32                         */
+
+/* partition_size values for paged_attention_decode besides a positive size */
+#define PKV_PARTITION_NONE 0  /* one wavefront per (sequence, KV head)        */
+#define PKV_PARTITION_AUTO (-1) /* balanced split of all blocks over the GPU  */
+
+/* Text describing the last non-OK status returned on the calling thread. */
+PKV_API const char *pagedkv_last_error(void);
+
+/* kv_append -- store the new tokens' K and V rows into the paged pools.
+ *
+ * Defined by: README table of contents "Why KV cache exists" / "Paged KV
+ * cache" and guide ch. 3 (each token's K and V are written once and looked
+ * up afterwards) and ch. 4 (pages of the cache addressed through a table).
+ *
+ * k_cache, v_cache  [num_blocks][Hkv][block_size][D] bf16, written in place.
+ * k_new, v_new      [T_new][Hkv][D] bf16, packed by sequence.
+ * block_tables      [B][max_blocks_per_seq] int32.
+ * context_lens      [B] int32, lengths AFTER the append.
+ * cu_new_lens       [B+1] int32 prefix sums of new tokens per sequence, or
+ *                   NULL for exactly one new token per sequence (T_new == B).
+ * New token t of sequence b (n_b new tokens) goes to logical position
+ * context_lens[b] - n_b + t.  The copy is bit-exact.  Rows whose slot falls
+ * outside the table or pool are not written.  Requires D % 8 == 0.
+ */
+PKV_API int kv_append(void *k_cache, void *v_cache, const void *k_new, const void *v_new,
+              const int32_t *block_tables, const int32_t *context_lens,
+              const int32_t *cu_new_lens, int32_t B, int32_t T_new, int32_t Hkv,
+              int32_t D, int32_t block_size, int32_t max_blocks_per_seq,
+              int32_t num_blocks, void *stream);
+
+/* Bytes of device workspace paged_attention_decode needs for these arguments
+ * (0 when no split is requested).  Pure function of its arguments; makes no
+ * HIP call.  Returns 0 for arguments decode would reject. */
+PKV_API size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv,
+                                             int32_t D, int32_t block_size,
+                                             int32_t max_context_len,
+                                             int32_t partition_size);
+
+/* paged_attention_decode -- one query token per sequence attends to all
+ * context_lens[b] cached tokens of its sequence.
+ *
+ * Defined by: README table of contents "Attention", "GQA", "Softmax",
+ * "Online softmax", "Paged Attention" and guide ch. 6 (decode reads the whole
+ * cache for one new token and is memory bound):
+ *     out[b][h] = sum_j softmax_j(scale * q[b][h] . k_j) v_j,
+ *     j over the sequence's tokens, k_j/v_j gathered through the block table.
+ *
+ * out           [B][Hq][D], bf16 or fp32 per out_dtype.
+ * q             [B][Hq][D] bf16.
+ * k_cache/v_cache, block_tables, context_lens as for kv_append.
+ * max_context_len  host-side upper bound of context_lens (sizes the grid;
+ *               larger lengths on the device are clamped to it).
+ * scale         multiplies q.k before the softmax (e.g. 1/sqrt(D)); finite.
+ * partition_size  PKV_PARTITION_NONE: each (sequence, KV head) in one
+ *               wavefront.  A positive multiple of block_size: each sequence
+ *               is split at multiples of that many tokens, partitions run in
+ *               parallel and a second kernel merges them by log-sum-exp.
+ *               PKV_PARTITION_AUTO: all blocks of the batch are cut into equal
+ *               shares, one per wavefront of a fixed grid, and streams cut
+ *               across shares are merged the same way.
+ * workspace     device scratch of at least
+ *               paged_attention_decode_workspace_size(...) bytes (may be NULL
+ *               when that is 0).  Its contents need no initialisation and
+ *               are meaningless after the call.
+ * This build implements D == 64, block_size == 16 and Hq == 4 * Hkv
+ * (PKV_ERR_UNSUPPORTED otherwise).  Empty contexts give zero rows.
+ */
+PKV_API int paged_attention_decode(void *out, int32_t out_dtype, const void *q,
+                           const void *k_cache, const void *v_cache,
+                           const int32_t *block_tables, const int32_t *context_lens,
+                           int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                           int32_t block_size, int32_t max_blocks_per_seq,
+                           int32_t num_blocks, int32_t max_context_len, float scale,
+                           int32_t partition_size, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* paged_attention_prefill_causal -- every prompt token attends to the cached
+ * tokens up to and including its own position.
+ *
+ * Defined by: README table of contents "Prefill vs decode", "Attention",
+ * "GQA", "Causal mask", "Online softmax", "Paged Attention" and guide ch. 6
+ * (prefill processes the whole prompt and is compute bound).  Query t of
+ * sequence b sits at position pos = context_lens[b] - q_len_b + t and sees
+ * keys 0..pos; the K/V of the prompt must already be in the pools (kv_append).
+ *
+ * out           [T_q][Hq][D], bf16 or fp32 per out_dtype.
+ * q             [T_q][Hq][D] bf16, packed by sequence.
+ * cu_q_lens     [B+1] int32 prefix sums of query tokens per sequence.
+ * max_q_len     host-side upper bound of the per-sequence query counts.
+ * Other arguments as for decode.  This build implements D == 64,
+ * block_size == 16 and Hq == 4 * Hkv.
+ */
+PKV_API int paged_attention_prefill_causal(void *out, int32_t out_dtype, const void *q,
+                                   const void *k_cache, const void *v_cache,
+                                   const int32_t *block_tables,
+                                   const int32_t *context_lens,
+                                   const int32_t *cu_q_lens, int32_t B, int32_t T_q,
+                                   int32_t Hq, int32_t Hkv, int32_t D,
+                                   int32_t block_size, int32_t max_blocks_per_seq,
+                                   int32_t num_blocks, int32_t max_q_len, float scale,
+                                   void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,1 +1,191 @@
-"""MI355X-native paged KV-cache attention (placeholder until the HIP library lands)."""
+"""MI355X-native paged KV-cache attention: Python binding of libpagedkv.so.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of libpagedkv.so (built for gfx950 by build.py); torch supplies the
+device memory and the current stream.  If the library is not built, every
+call raises -- there is no CPU fallback.
+
+Entry points (same names as the C ABI in include/pagedkv.h):
+    kv_append(k_cache, v_cache, k_new, v_new, block_tables, context_lens,
+              cu_new_lens=None)
+    paged_attention_decode(out, q, k_cache, v_cache, block_tables,
+              context_lens, scale, max_context_len, partition_size=AUTO,
+              workspace=None)
+    paged_attention_prefill_causal(out, q, k_cache, v_cache, block_tables,
+              context_lens, cu_q_lens, scale, max_q_len)
+    paged_attention_decode_workspace_size(...)
+"""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libpagedkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = -1
+PKV_ERR_UNSUPPORTED = -2
+PKV_ERR_WORKSPACE = -3
+PKV_ERR_HIP = -4
+PKV_OUT_BF16 = 0
+PKV_OUT_F32 = 1
+PARTITION_NONE = 0
+PARTITION_AUTO = -1
+
+# every symbol include/pagedkv.h declares
+ABI_SYMBOLS = ("pagedkv_last_error", "kv_append", "paged_attention_decode_workspace_size",
+               "paged_attention_decode", "paged_attention_prefill_causal")
+
+_lib = None
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+def load_library():
+    """Load libpagedkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python __graft_entry__.py` "
+                           "(hipcc --offload-arch=gfx950); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    lib.pagedkv_last_error.argtypes = []
+    lib.pagedkv_last_error.restype = ctypes.c_char_p
+    lib.kv_append.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
+    lib.kv_append.restype = ctypes.c_int
+    lib.paged_attention_decode_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.paged_attention_decode_workspace_size.restype = Z
+    lib.paged_attention_decode.argtypes = [P, I, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I,
+                                           P, Z, P]
+    lib.paged_attention_decode.restype = ctypes.c_int
+    lib.paged_attention_prefill_causal.argtypes = [P, I, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                                   I, I, F, P]
+    lib.paged_attention_prefill_causal.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load_library().pagedkv_last_error().decode()
+
+
+def _check(rc):
+    if rc != PKV_OK:
+        raise PagedKVError(rc, last_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream():
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _out_dtype(out):
+    torch = _torch()
+    if out.dtype == torch.bfloat16:
+        return PKV_OUT_BF16
+    if out.dtype == torch.float32:
+        return PKV_OUT_F32
+    raise TypeError("out must be bfloat16 or float32")
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, block_tables, context_lens, cu_new_lens=None):
+    """Write new K/V rows [T_new][Hkv][D] into the pools [N][Hkv][bs][D] in place."""
+    torch = _torch()
+    N, Hkv, bs, D = k_cache.shape
+    B, maxb = block_tables.shape
+    T_new = k_new.shape[0]
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k/v shapes differ")
+    if tuple(k_new.shape[1:]) != (Hkv, D):
+        raise ValueError("k_new must be [T_new][Hkv][D]")
+    cu_ptr = None
+    if cu_new_lens is not None:
+        if cu_new_lens.numel() != B + 1:
+            raise ValueError("cu_new_lens must have B+1 entries")
+        cu_ptr = _dev(cu_new_lens, torch.int32, "cu_new_lens")
+    _check(load_library().kv_append(
+        _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
+        _dev(k_new, torch.bfloat16, "k_new"), _dev(v_new, torch.bfloat16, "v_new"),
+        _dev(block_tables, torch.int32, "block_tables"),
+        _dev(context_lens, torch.int32, "context_lens"), cu_ptr, B, T_new, Hkv, D, bs, maxb, N,
+        _stream()))
+
+
+def paged_attention_decode_workspace_size(B, Hq, Hkv, D, block_size, max_context_len,
+                                          partition_size=PARTITION_AUTO) -> int:
+    return int(load_library().paged_attention_decode_workspace_size(
+        B, Hq, Hkv, D, block_size, max_context_len, partition_size))
+
+
+def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                           max_context_len, partition_size=PARTITION_AUTO, workspace=None):
+    """out[B][Hq][D] (bf16 or fp32) = paged decode attention of q[B][Hq][D].
+
+    workspace: a device uint8 tensor of at least
+    paged_attention_decode_workspace_size(...) bytes when a split is used."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    N, Hkv, bs, _ = k_cache.shape
+    maxb = block_tables.shape[1]
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B][Hq][D]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    _check(load_library().paged_attention_decode(
+        _dev(out, out.dtype, "out"), _out_dtype(out), _dev(q, torch.bfloat16, "q"),
+        _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
+        _dev(block_tables, torch.int32, "block_tables"),
+        _dev(context_lens, torch.int32, "context_lens"), B, Hq, Hkv, D, bs, maxb, N,
+        int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes, _stream()))
+
+
+def paged_attention_prefill_causal(out, q, k_cache, v_cache, block_tables, context_lens,
+                                   cu_q_lens, scale, max_q_len):
+    """out[T][Hq][D] = causal paged prefill attention of packed q[T][Hq][D]."""
+    torch = _torch()
+    T, Hq, D = q.shape
+    N, Hkv, bs, _ = k_cache.shape
+    B, maxb = block_tables.shape
+    if tuple(out.shape) != (T, Hq, D):
+        raise ValueError("out must be [T][Hq][D]")
+    if cu_q_lens.numel() != B + 1:
+        raise ValueError("cu_q_lens must have B+1 entries")
+    _check(load_library().paged_attention_prefill_causal(
+        _dev(out, out.dtype, "out"), _out_dtype(out), _dev(q, torch.bfloat16, "q"),
+        _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
+        _dev(block_tables, torch.int32, "block_tables"),
+        _dev(context_lens, torch.int32, "context_lens"),
+        _dev(cu_q_lens, torch.int32, "cu_q_lens"), B, T, Hq, Hkv, D, bs, maxb, N,
+        int(max_q_len), float(scale), _stream()))
+
+
+def decode_workspace(B, Hq, Hkv, D, block_size, max_context_len, partition_size, device):
+    """Allocate (with torch) the workspace a decode call needs, or None."""
+    n = paged_attention_decode_workspace_size(B, Hq, Hkv, D, block_size, max_context_len,
+                                              partition_size)
+    if n == 0:
+        return None
+    return _torch().empty(n, dtype=_torch().uint8, device=device)

@@ -1,0 +1,221 @@
+// api.cpp -- the extern "C" entry points of libpagedkv.so declared in
+// include/pagedkv.h.  Every argument is validated on the host before any HIP
+// call (so invalid arguments never reach the device); then the work is
+// enqueued on the caller's stream and the launch status is returned.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "launch.h"
+#include "pagedkv.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kD = 64, kBS = 16, kGroup = 4;
+
+// Decode mode and split geometry for the given arguments.
+struct DecodePlan {
+  int mode, part_blocks, parts_max;
+  size_t records, bytes;
+};
+
+int plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                int32_t max_context_len, int32_t partition_size, DecodePlan* plan) {
+  if (B < 0) return fail(PKV_ERR_INVALID_ARG, "B must be >= 0 (got %d)", B);
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(PKV_ERR_INVALID_ARG, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  if (D != kD) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not implemented (64 only)", D);
+  if (block_size != kBS)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d not implemented (16 only)", block_size);
+  if (Hq != kGroup * Hkv)
+    return fail(PKV_ERR_UNSUPPORTED, "GQA group %d not implemented (Hq == 4*Hkv only)", Hq / Hkv);
+  if (max_context_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "max_context_len must be >= 0 (got %d)", max_context_len);
+  plan->mode = pkv::kWhole;
+  plan->part_blocks = 0;
+  plan->parts_max = 1;
+  if (partition_size == PKV_PARTITION_AUTO) {
+    if (B > pkv::kAutoMaxBatch)
+      return fail(PKV_ERR_UNSUPPORTED, "automatic split handles B <= %d (got %d)",
+                  pkv::kAutoMaxBatch, B);
+    plan->mode = pkv::kAuto;
+  } else if (partition_size > 0) {
+    if (partition_size % block_size != 0)
+      return fail(PKV_ERR_UNSUPPORTED, "partition_size %d is not a multiple of block_size %d",
+                  partition_size, block_size);
+    const int parts = (int)(((int64_t)max_context_len + partition_size - 1) / partition_size);
+    if (parts > 1) {
+      plan->mode = pkv::kFixed;
+      plan->part_blocks = partition_size / block_size;
+      plan->parts_max = parts;
+    }
+  } else if (partition_size != PKV_PARTITION_NONE) {
+    return fail(PKV_ERR_INVALID_ARG, "partition_size %d: use > 0, 0 (none) or -1 (auto)",
+                partition_size);
+  }
+  plan->records = pkv::decode_records(plan->mode, B, Hkv, plan->parts_max);
+  plan->bytes = plan->records * (pkv::kRecordFloats + 8) * sizeof(float);
+  if (plan->mode == pkv::kAuto) plan->bytes += (size_t)(B + 2) * sizeof(int32_t);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pagedkv_last_error(void) { return g_err; }
+
+int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+              const int32_t* block_tables, const int32_t* context_lens,
+              const int32_t* cu_new_lens, int32_t B, int32_t T_new, int32_t Hkv, int32_t D,
+              int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+              void* stream) {
+  if (B < 0 || T_new < 0)
+    return fail(PKV_ERR_INVALID_ARG, "B (%d) and T_new (%d) must be >= 0", B, T_new);
+  if (B == 0 || T_new == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (Hkv <= 0 || D <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "Hkv, D, block_size, max_blocks_per_seq, num_blocks must be > 0");
+  if (D % 8 != 0) return fail(PKV_ERR_UNSUPPORTED, "D %d is not a multiple of 8", D);
+  if (!cu_new_lens && T_new != B)
+    return fail(PKV_ERR_INVALID_ARG, "cu_new_lens is NULL but T_new (%d) != B (%d)", T_new, B);
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_ERR_INVALID_ARG, "pools and new rows must be 16-byte aligned");
+  if ((int64_t)T_new * 2 * Hkv * (D / 8) / 256 >= INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "too many new rows for one launch");
+  pkv::KvAppendArgs a{k_cache, v_cache, k_new, v_new, block_tables, context_lens, cu_new_lens,
+                      B, T_new, Hkv, D, block_size, max_blocks_per_seq, num_blocks};
+  return hip_status(pkv::launch_kv_append(a, (hipStream_t)stream), "kv_append launch");
+}
+
+size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                             int32_t block_size, int32_t max_context_len,
+                                             int32_t partition_size) {
+  DecodePlan plan;
+  if (plan_decode(B, Hq, Hkv, D, block_size, max_context_len, partition_size, &plan) != PKV_OK)
+    return 0;
+  return plan.bytes;
+}
+
+int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t block_size, int32_t max_blocks_per_seq,
+                           int32_t num_blocks, int32_t max_context_len, float scale,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  DecodePlan plan;
+  int rc = plan_decode(B, Hq, Hkv, D, block_size, max_context_len, partition_size, &plan);
+  if (rc != PKV_OK) return rc;
+  if (B == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (out_dtype != PKV_OUT_BF16 && out_dtype != PKV_OUT_F32)
+    return fail(PKV_ERR_INVALID_ARG, "out_dtype %d is neither PKV_OUT_BF16 nor PKV_OUT_F32", out_dtype);
+  if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq and num_blocks must be > 0");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "out, q and the pools must be 16-byte aligned");
+  if (plan.bytes > 0) {
+    if (!workspace || workspace_bytes < plan.bytes)
+      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.bytes,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned16(workspace)) return fail(PKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  }
+  if ((int64_t)B * Hkv * plan.parts_max / 4 >= INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "too many (sequence, head, partition) units for one launch");
+  float* ws = static_cast<float*>(workspace);
+  pkv::DecodeArgs a;
+  a.out = out;
+  a.out_f32 = out_dtype == PKV_OUT_F32;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  a.mode = plan.mode;
+  a.part_blocks = plan.part_blocks;
+  a.parts_max = plan.parts_max;
+  a.ws_o = plan.bytes ? ws : nullptr;
+  a.ws_ml = plan.bytes ? ws + plan.records * pkv::kRecordFloats : nullptr;
+  return hip_status(pkv::launch_decode(a, (hipStream_t)stream), "paged_attention_decode launch");
+}
+
+int paged_attention_prefill_causal(void* out, int32_t out_dtype, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   const int32_t* cu_q_lens, int32_t B, int32_t T_q, int32_t Hq,
+                                   int32_t Hkv, int32_t D, int32_t block_size,
+                                   int32_t max_blocks_per_seq, int32_t num_blocks,
+                                   int32_t max_q_len, float scale, void* stream) {
+  if (B < 0 || T_q < 0)
+    return fail(PKV_ERR_INVALID_ARG, "B (%d) and T_q (%d) must be >= 0", B, T_q);
+  if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
+    return fail(PKV_ERR_INVALID_ARG, "Hq (%d) must be a positive multiple of Hkv (%d)", Hq, Hkv);
+  if (D != kD) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not implemented (64 only)", D);
+  if (block_size != kBS)
+    return fail(PKV_ERR_UNSUPPORTED, "block_size %d not implemented (16 only)", block_size);
+  if (Hq != kGroup * Hkv)
+    return fail(PKV_ERR_UNSUPPORTED, "GQA group %d not implemented (Hq == 4*Hkv only)", Hq / Hkv);
+  if (max_q_len < 0) return fail(PKV_ERR_INVALID_ARG, "max_q_len must be >= 0");
+  if (B == 0 || T_q == 0 || max_q_len == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !cu_q_lens)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (out_dtype != PKV_OUT_BF16 && out_dtype != PKV_OUT_F32)
+    return fail(PKV_ERR_INVALID_ARG, "out_dtype %d is neither PKV_OUT_BF16 nor PKV_OUT_F32", out_dtype);
+  if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq and num_blocks must be > 0");
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "out, q and the pools must be 16-byte aligned");
+  pkv::PrefillArgs a;
+  a.out = out;
+  a.out_f32 = out_dtype == PKV_OUT_F32;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.cu_q_lens = cu_q_lens;
+  a.B = B;
+  a.T_q = T_q;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_q_len = max_q_len;
+  a.scale = scale;
+  return hip_status(pkv::launch_prefill(a, (hipStream_t)stream),
+                    "paged_attention_prefill_causal launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,69 @@
+// launch.h -- internal kernel-launch interface of libpagedkv.so (host side).
+// Arguments arrive here already validated by the C-ABI layer in api.hip.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct KvAppendArgs {
+  void* k_cache;
+  void* v_cache;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* cu_new_lens;
+  int32_t B, T_new, Hkv, D, block_size, max_blocks_per_seq, num_blocks;
+};
+hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
+
+// Decode work decomposition (see decode.hip).
+enum DecodeMode : int { kWhole = 0, kFixed = 1, kAuto = 2 };
+
+// Fixed grid of wavefronts used by the balanced split: 8 per CU of a
+// 256-CU MI355X.  Part of the workspace-size formula, so a constant.
+constexpr int kAutoWaves = 2048;
+// Largest batch the balanced split handles (per-sequence prefix in LDS).
+constexpr int kAutoMaxBatch = 4096;
+
+// One split record: normalised partial output for the 4 query heads of a
+// KV group (4 x 64 fp32) followed, in a separate array, by (m, l) per head.
+constexpr int kRecordFloats = 4 * 64;
+
+struct DecodeArgs {
+  void* out;
+  int32_t out_f32;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t B, Hq, Hkv, max_blocks_per_seq, num_blocks, max_context_len;
+  float scale;
+  int32_t mode;            // DecodeMode
+  int32_t part_blocks;     // kFixed: blocks per partition
+  int32_t parts_max;       // kFixed: partitions per stream upper bound
+  float* ws_o;             // records x kRecordFloats
+  float* ws_ml;            // records x 4 heads x (m, l)
+};
+size_t decode_records(int32_t mode, int32_t B, int32_t Hkv, int32_t parts_max);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct PrefillArgs {
+  void* out;
+  int32_t out_f32;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* cu_q_lens;
+  int32_t B, T_q, Hq, Hkv, max_blocks_per_seq, num_blocks, max_q_len;
+  float scale;
+};
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pkv

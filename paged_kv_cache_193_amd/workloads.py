@@ -90,7 +90,7 @@ def tables_from_permutation(gen: torch.Generator, lens: torch.Tensor, block_size
     pool_ids = num_blocks - 1 if reserve_last else num_blocks
     if int(need.sum()) > pool_ids:
         raise ValueError("pool too small for the drawn lengths")
-    if int(need.max(initial=0)) > max_blocks:
+    if len(need) and int(need.max()) > max_blocks:
         raise ValueError("max_blocks too small for the drawn lengths")
     perm = torch.randperm(pool_ids, generator=gen).to(torch.int32)
     tables = torch.full((len(lens), max_blocks), filler, dtype=torch.int32)
@@ -130,7 +130,7 @@ class PagedCase:
 
     @property
     def max_context_len(self) -> int:
-        return int(self.context_lens.max(initial=0))
+        return int(self.context_lens.max()) if len(self.context_lens) else 0
 
 
 def poison_unused(case: PagedCase, value=float("nan")) -> None:
@@ -200,7 +200,7 @@ def prefill_case(seed: Optional[int] = None, prompts: Optional[List[int]] = None
     B, D, bs = len(prompts), HEAD_DIM, BLOCK_SIZE
     q_lens = torch.tensor(prompts, dtype=torch.int32)
     lens = q_lens + torch.tensor(history, dtype=torch.int32)
-    max_blocks = int(blocks_needed(lens, bs).max(initial=1))
+    max_blocks = max(1, int(blocks_needed(lens, bs).max())) if len(lens) else 1
     tables = tables_from_permutation(g, lens, bs, N, max_blocks, filler=N - 1)
     T = int(q_lens.sum())
     cu = torch.zeros(B + 1, dtype=torch.int32)
