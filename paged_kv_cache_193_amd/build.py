@@ -26,9 +26,10 @@ COMMON = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJ_DIR, src + ".o")
-    cmd = ["hipcc", *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, verbose: bool, defines=(), obj_dir=OBJ_DIR) -> str:
+    obj = os.path.join(obj_dir, src + ".o")
+    cmd = ["hipcc", *COMMON, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src),
+           "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     if verbose:
@@ -42,17 +43,21 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(verbose: bool = False, defines=(), lib: str = LIB) -> str:
+    """Compile every source and link `lib`.  `defines` (NAME=VALUE strings)
+    override tuning constants; the default build uses none."""
+    obj_dir = OBJ_DIR if not defines else os.path.join(
+        OBJ_DIR, "_".join(d.replace("=", "") for d in defines))
+    os.makedirs(obj_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
+        objs = list(ex.map(lambda s: _compile(s, verbose, defines, obj_dir), SOURCES))
+    cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", lib + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(lib + ".tmp", lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -47,8 +47,10 @@ namespace {
 constexpr int kD = 64;
 constexpr int kBS = 16;
 constexpr int kWaves = 4;        // wavefronts per workgroup
-constexpr int kRing = 4;         // K/V blocks in flight per wavefront
-constexpr float kLazy = 8.0f;    // rescale threshold, log2 units
+#ifndef PKV_DECODE_RING
+#define PKV_DECODE_RING 4
+#endif
+constexpr int kRing = PKV_DECODE_RING;  // K/V blocks in flight per wavefront
 
 struct BlockRegs {
   u32x4 ka, kb, va, vb;  // tokens grp and grp+8, head_dim chunk i
@@ -103,60 +105,41 @@ __device__ __forceinline__ int issue_block(BlockRegs& r, const Params& p, int ph
   return nv;
 }
 
-template <bool kTail>
-__device__ __forceinline__ void consume_block(LaneState& st, const BlockRegs& r,
-                                              const uint32_t (&qv)[4][4], float scale_log2,
-                                              int n_valid, bool quad1, int grp) {
-  // partial dots over this lane's 8-wide chunk: token s, head slot j
+// Score of this lane's own (head c, token) pair for one block, log2 units:
+// partial dots over the lane's 8-wide chunk for 2 tokens x 4 head slots,
+// then a reduce-scatter over the 8 lanes of the group.
+__device__ __forceinline__ float block_score(const BlockRegs& r, const uint32_t (&qv)[4][4],
+                                             float scale_log2, bool quad1) {
   float pd[2][4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float a = 0.f, b = 0.f;
+    float a = dot2_bf16(qv[j][0], r.ka[0], 0.f);
+    float b = dot2_bf16(qv[j][0], r.kb[0], 0.f);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 1; w < 4; ++w) {
       a = dot2_bf16(qv[j][w], r.ka[w], a);
       b = dot2_bf16(qv[j][w], r.kb[w], b);
     }
     pd[0][j] = a;
     pd[1][j] = b;
   }
-  // reduce-scatter over the 8 lanes of the group
   float t[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    float r0 = pd[s][0] + dpp<kQuadXor2>(pd[s][2]);
-    float r1 = pd[s][1] + dpp<kQuadXor2>(pd[s][3]);
+    const float r0 = pd[s][0] + dpp<kQuadXor2>(pd[s][2]);
+    const float r1 = pd[s][1] + dpp<kQuadXor2>(pd[s][3]);
     t[s] = r0 + dpp<kQuadXor1>(r1);
   }
   const float keep = quad1 ? t[1] : t[0];
   const float send = quad1 ? t[0] : t[1];
-  float x = (keep + dpp<kRowHalfMirror>(send)) * scale_log2;
-  const int tok = quad1 ? grp + 8 : grp;
-  if (kTail && tok >= n_valid) x = -INFINITY;
+  return (keep + dpp<kRowHalfMirror>(send)) * scale_log2;
+}
 
-  // lazy online-softmax update
-  const float mx = fmaxf(x, dpp<kRowHalfMirror>(x));
-  const bool need = mx > st.m + kLazy;
-  if (__builtin_amdgcn_ballot_w64(need)) {
-    const float m_new = need ? mx : st.m;
-    const float alpha = need ? __builtin_amdgcn_exp2f(st.m - m_new) : 1.0f;
-    st.m = m_new;
-    st.l *= alpha;
-    const float a1 = dpp<kQuadXor1>(alpha), a2 = dpp<kQuadXor2>(alpha),
-                a3 = dpp<kQuadXor3>(alpha);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      st.acc[0][e] *= alpha;
-      st.acc[1][e] *= a1;
-      st.acc[2][e] *= a2;
-      st.acc[3][e] *= a3;
-    }
-  }
-  float pw = __builtin_amdgcn_exp2f(x - st.m);
-  if (kTail && tok >= n_valid) pw = 0.f;
-  st.l += pw;
-
-  // weights of tokens (grp, grp+8) for this lane's head, then for each slot
+// P.V of one block: weights p of this lane's (head c, own token), V rows of
+// tokens grp and grp+8 (zeroed where not valid, so 0 * NaN never happens).
+template <bool kMasked>
+__device__ __forceinline__ void block_pv(LaneState& st, const BlockRegs& r, float pw,
+                                         bool quad1, bool va_ok, bool vb_ok) {
   const float pm = dpp<kRowHalfMirror>(pw);
   const uint32_t p2 = pack_bf16(quad1 ? pm : pw, quad1 ? pw : pm);
   uint32_t ps[4];
@@ -164,11 +147,10 @@ __device__ __forceinline__ void consume_block(LaneState& st, const BlockRegs& r,
   ps[1] = dpp_u32<kQuadXor1>(p2);
   ps[2] = dpp_u32<kQuadXor2>(p2);
   ps[3] = dpp_u32<kQuadXor3>(p2);
-
   u32x4 va = r.va, vb = r.vb;
-  if (kTail) {
-    if (grp >= n_valid) va = u32x4{0, 0, 0, 0};
-    if (grp + 8 >= n_valid) vb = u32x4{0, 0, 0, 0};
+  if (kMasked) {
+    if (!va_ok) va = u32x4{0, 0, 0, 0};
+    if (!vb_ok) vb = u32x4{0, 0, 0, 0};
   }
   uint32_t v2[8];
 #pragma unroll
@@ -183,11 +165,20 @@ __device__ __forceinline__ void consume_block(LaneState& st, const BlockRegs& r,
 }
 
 // Run blocks [j0, j1) of stream (b, g) through one wavefront.
+//
+// The blocks go through a ring of kRing register slots in groups of kRing:
+// the scores of a whole group are formed first, the running max moves once
+// per group (one rescale of the accumulator, no branch), then P.V runs block
+// by block and each slot is refilled with the block kRing ahead as soon as its
+// V is consumed.  Every group issues exactly kRing block loads (past the
+// segment end the last block is re-read, a cache hit marked invalid), so the
+// hardware wait counts stay exact.
 __device__ __forceinline__ void run_segment(LaneState& st, const Params& p, int b, int g,
                                             int j0, int j1, int ctx, int lane) {
   const int grp = lane >> 3, i = lane & 7;
   const bool quad1 = (i & 4) != 0;
   const int c = quad1 ? ((i & 3) ^ 3) : (i & 3);
+  const int own_tok = quad1 ? grp + 8 : grp;
 
   // this lane's query chunks, head order slot j -> head j ^ c
   uint32_t qv[4][4];
@@ -210,31 +201,60 @@ __device__ __forceinline__ void run_segment(LaneState& st, const Params& p, int 
   const int lane_off = grp * kD + 8 * i;
   const int nb = j1 - j0;
   const int last = j1 - 1;
-  // Block ids: lane k of `tab` holds the id of block tab_base + k (clamped to
-  // the segment), read with readlane when the block is issued; the window is
-  // refilled once per 64 blocks.
+  // block ids: lane k of `tab` holds the id of block tab_base + k (clamped to
+  // the segment), read with readlane; refilled once per 64 blocks
   int tab_base = j0;
   int tab = trow[j0 + lane < last ? j0 + lane : last];
-  // K/V of kRing blocks in flight.  Every step of the loop issues exactly
-  // kRing blocks (past the segment end it re-reads the last block, a cache
-  // hit that is never consumed), so the hardware wait counts stay exact.
+
   BlockRegs ring[kRing];
   int nvalid[kRing];
 #pragma unroll
   for (int s = 0; s < kRing; ++s) {
     const int j = j0 + s < last ? j0 + s : last;
-    nvalid[s] = issue_block(ring[s], p, __builtin_amdgcn_readlane(tab, j - tab_base), g, j,
-                            ctx, lane_off);
+    const int nv = issue_block(ring[s], p, __builtin_amdgcn_readlane(tab, j - tab_base), g, j,
+                               ctx, lane_off);
+    nvalid[s] = s < nb ? nv : 0;
   }
+
   for (int base = 0; base < nb; base += kRing) {
+    bool full = true;
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) full = full && nvalid[s] == kBS;
+    float x[kRing];
 #pragma unroll
     for (int s = 0; s < kRing; ++s) {
-      if (base + s < nb) {
-        if (nvalid[s] == kBS)
-          consume_block<false>(st, ring[s], qv, p.scale_log2, kBS, quad1, grp);
-        else
-          consume_block<true>(st, ring[s], qv, p.scale_log2, nvalid[s], quad1, grp);
-      }
+      x[s] = block_score(ring[s], qv, p.scale_log2, quad1);
+      if (!full && own_tok >= nvalid[s]) x[s] = -INFINITY;
+    }
+    // one max per group, shared by the mirror pair (same head, tokens t, t+8)
+    float mx = x[0];
+#pragma unroll
+    for (int s = 1; s < kRing; ++s) mx = fmaxf(mx, x[s]);
+    mx = fmaxf(mx, dpp<kRowHalfMirror>(mx));
+    const float m_new = fmaxf(st.m, mx);
+    // no valid token yet on this lane pair: keep everything at zero weight
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+    st.m = m_new;
+    st.l *= alpha;
+    const float a1 = dpp<kQuadXor1>(alpha), a2 = dpp<kQuadXor2>(alpha),
+                a3 = dpp<kQuadXor3>(alpha);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      st.acc[0][e] *= alpha;
+      st.acc[1][e] *= a1;
+      st.acc[2][e] *= a2;
+      st.acc[3][e] *= a3;
+    }
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+      const float pw = __builtin_amdgcn_exp2f(x[s] - m_use);  // 0 for x = -inf
+      st.l += pw;
+      if (full)
+        block_pv<false>(st, ring[s], pw, quad1, true, true);
+      else
+        block_pv<true>(st, ring[s], pw, quad1, grp < nvalid[s], grp + 8 < nvalid[s]);
+      // refill this slot with the block kRing ahead
       const int jn = j0 + base + s + kRing;
       const int j = jn < last ? jn : last;
       if (j - tab_base >= 64) {
@@ -244,8 +264,9 @@ __device__ __forceinline__ void run_segment(LaneState& st, const Params& p, int 
         // carries no wait for this load
         __builtin_amdgcn_s_waitcnt(0x0F70);
       }
-      nvalid[s] = issue_block(ring[s], p, __builtin_amdgcn_readlane(tab, j - tab_base), g, j,
-                              ctx, lane_off);
+      const int nv = issue_block(ring[s], p, __builtin_amdgcn_readlane(tab, j - tab_base), g, j,
+                                 ctx, lane_off);
+      nvalid[s] = jn < j1 ? nv : 0;
     }
   }
 }
@@ -439,19 +460,27 @@ decode_auto_kernel(Params p) {
   }
 }
 
-// Log-sum-exp merge of split records, one workgroup per stream (b, g);
-// thread -> (head h = tid / 64, d = tid % 64).
+// Log-sum-exp merge of split records, one workgroup per stream (b, g).
+// The (m, l) pairs of up to kMergeChunk records x 4 heads are staged in LDS
+// with one parallel load; then thread (head h = tid / 64, d = tid % 64)
+// folds the chunk into its running (M, numerator, denominator) with
+// independent loads of the records' outputs.
+constexpr int kMergeChunk = 256;
+
 template <int kMode>
 __global__ void __launch_bounds__(256)
 decode_merge_kernel(Params p) {
+  __shared__ float sm[kMergeChunk][4];
+  __shared__ float sl[kMergeChunk][4];
+  __shared__ int64_t srec[kMergeChunk];
   const int stream = blockIdx.x;
   const int b = stream / p.Hkv;
   const int g = stream - b * p.Hkv;
-  const int h = threadIdx.x >> 6;
-  const int d = threadIdx.x & 63;
-  int first, count;
+  const int tid = threadIdx.x;
+  const int h = tid >> 6;
+  const int d = tid & 63;
+  int count, first = 0, w0 = 0;
   int64_t start_x = 0, C = 1;
-  int w0 = 0;
   if (kMode == kFixed) {
     const int ctx = eff_ctx(p, b);
     const int nb = (ctx + kBS - 1) / kBS;
@@ -459,44 +488,53 @@ decode_merge_kernel(Params p) {
     first = stream * p.parts_max;
   } else {
     const int pb = p.ws_pfx[b], nb = p.ws_pfx[b + 1] - pb;
-    C = p.ws_pfx[p.B + 1];
-    if (nb == 0) {
-      count = 0;
-      first = 0;
-    } else {
-      start_x = (int64_t)p.Hkv * pb + (int64_t)g * nb;
-      w0 = (int)(start_x / C);
-      const int w1 = (int)((start_x + nb - 1) / C);
-      count = w1 - w0 + 1;
-      first = 0;
-    }
     if (nb == 0) {  // empty context: zero rows (no wavefront saw this stream)
-      if (threadIdx.x < 64) write_zero_rows(p, b, g, threadIdx.x);
+      if (tid < 64) write_zero_rows(p, b, g, tid);
       return;
     }
+    C = p.ws_pfx[p.B + 1];
+    start_x = (int64_t)p.Hkv * pb + (int64_t)g * nb;
+    w0 = (int)(start_x / C);
+    const int w1 = (int)((start_x + nb - 1) / C);
+    count = w1 - w0 + 1;
   }
   if (count <= 1) return;  // written directly by the decode kernel
 
-  auto record_of = [&](int k) -> int64_t {
-    if (kMode == kFixed) return first + k;
-    const int w = w0 + k;
-    return 2LL * w + ((k == 0 && start_x > (int64_t)w0 * C) ? 1 : 0);
-  };
-  float M = -INFINITY;
-  for (int k = 0; k < count; ++k) {
-    const int64_t r = record_of(k);
-    const float l = p.ws_ml[(r * 4 + h) * 2 + 1];
-    const float m = p.ws_ml[(r * 4 + h) * 2 + 0];
-    if (l > 0.f) M = fmaxf(M, m);
-  }
-  float num = 0.f, den = 0.f;
-  for (int k = 0; k < count; ++k) {
-    const int64_t r = record_of(k);
-    const float l = p.ws_ml[(r * 4 + h) * 2 + 1];
-    if (!(l > 0.f)) continue;
-    const float wgt = l * __builtin_amdgcn_exp2f(p.ws_ml[(r * 4 + h) * 2 + 0] - M);
-    num += wgt * p.ws_o[r * kRecordFloats + h * kD + d];
-    den += wgt;
+  float M = -INFINITY, num = 0.f, den = 0.f;
+  for (int k0 = 0; k0 < count; k0 += kMergeChunk) {
+    const int n = count - k0 < kMergeChunk ? count - k0 : kMergeChunk;
+    __syncthreads();
+    for (int idx = tid; idx < n * 4; idx += 256) {
+      const int k = idx >> 2, hh = idx & 3;
+      int64_t r;
+      if (kMode == kFixed) {
+        r = first + k0 + k;
+      } else {
+        const int w = w0 + k0 + k;
+        r = 2LL * w + ((k0 + k == 0 && start_x > (int64_t)w0 * C) ? 1 : 0);
+      }
+      if (hh == 0) srec[k] = r;
+      sm[k][hh] = p.ws_ml[(r * 4 + hh) * 2 + 0];
+      sl[k][hh] = p.ws_ml[(r * 4 + hh) * 2 + 1];
+    }
+    __syncthreads();
+    float Mc = -INFINITY;
+    for (int k = 0; k < n; ++k)
+      if (sl[k][h] > 0.f) Mc = fmaxf(Mc, sm[k][h]);
+    if (Mc == -INFINITY) continue;
+    const float Mn = fmaxf(M, Mc);
+    const float rescale = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+    num *= rescale;
+    den *= rescale;
+    M = Mn;
+#pragma unroll 8
+    for (int k = 0; k < n; ++k) {
+      const float l = sl[k][h];
+      const float wgt = l > 0.f ? l * __builtin_amdgcn_exp2f(sm[k][h] - M) : 0.f;
+      const float o = p.ws_o[srec[k] * kRecordFloats + h * kD + d];
+      num += wgt * o;
+      den += wgt;
+    }
   }
   const float o = den > 0.f ? num / den : 0.f;
   const int64_t row = ((int64_t)b * p.Hq + 4 * g + h) * kD + d;

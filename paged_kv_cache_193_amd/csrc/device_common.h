@@ -43,12 +43,12 @@ enum : int {
 
 template <int kCtrl>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, false));
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), kCtrl, 0xf, 0xf, true));
 }
 template <int kCtrl>
 __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xf, 0xf, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kCtrl, 0xf, 0xf, true);
 }
 
 // Value of x held by lane (lane ^ mask) for any mask < 64 (ds_bpermute).

@@ -25,7 +25,10 @@ enum DecodeMode : int { kWhole = 0, kFixed = 1, kAuto = 2 };
 
 // Fixed grid of wavefronts used by the balanced split: 8 per CU of a
 // 256-CU MI355X.  Part of the workspace-size formula, so a constant.
-constexpr int kAutoWaves = 2048;
+#ifndef PKV_AUTO_WAVES
+#define PKV_AUTO_WAVES 2048
+#endif
+constexpr int kAutoWaves = PKV_AUTO_WAVES;
 // Largest batch the balanced split handles (per-sequence prefix in LDS).
 constexpr int kAutoMaxBatch = 4096;
 

@@ -1,8 +1,328 @@
-// prefill.hip -- causal paged prefill (MFMA path): not yet implemented.
+// prefill.hip -- causal paged prefill: every prompt token attends to the
+// cached tokens up to and including its own position, reading K/V through the
+// block table (tiny-vllm README, table of contents "Prefill vs decode",
+// "Attention", "GQA", "Causal mask", "Online softmax", "Paged Attention";
+// nano-vLLM guide announcement ch. 6: prefill is compute bound).  Here the
+// path is a dense contraction, so Q.K^T and P.V run on CDNA4 bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
+//
+// Work unit: one workgroup per (64-row query tile, sequence b, KV group g);
+// its 4 wavefronts are the 4 query heads of the group, so every K/V tile
+// staged in LDS serves all of them (GQA).  Each wavefront holds, in registers,
+//   S^T[64 keys][64 q]   = K . Q^T       (4 MFMA tiles of 32x32)
+//   O^T[64 d][64 q]     += V^T . P^T     (4 MFMA tiles of 32x32)
+// The MFMA accumulator layout puts one query column and 16 keys in a lane
+// (rows 8*(r/4) + 4*(lane/32) + r%4, column lane%32), which is exactly the
+// layout P^T needs as the B operand of the next product: the softmax runs on
+// the scores where they are and no lane exchange is needed for P.  The row
+// statistics (max, sum) are per query column: in-lane over 32 keys plus one
+// exchange with lane^32.
+//
+// LDS per workgroup, double buffered: K tile [64 keys][64 d] row major and
+// V^T tile [64 d][64 keys] (the B-side key index must run along registers,
+// so V is transposed once per tile here and read back 8 bytes at a time).
+// Rows are padded to spread LDS banks.  Tiles past the context are zero
+// filled (never read from the pools), so 0 * NaN cannot reach the MFMA.
+//
+// Causal rule: query row t of a prompt of q_len tokens whose sequence holds
+// context_len tokens sits at position context_len - q_len + t and sees keys
+// 0..pos.  Key tiles entirely below the first row's position need no mask;
+// only diagonal tiles are masked.  Query tiles are launched heaviest first
+// and the KV group is the fastest-varying grid index (one KV head per XCD's
+// L2 for the 8-head case).
+#include "device_common.h"
 #include "launch.h"
 
 namespace pkv {
 
-hipError_t launch_prefill(const PrefillArgs&, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kD = 64;
+constexpr int kBS = 16;
+constexpr int kTile = 64;          // query rows per workgroup and keys per K/V tile
+constexpr int kKRow = kD + 8;      // K tile row stride (bf16 elements): 144 bytes
+constexpr int kVRow = kTile + 4;   // V^T tile row stride (bf16 elements): 136 bytes
+
+struct PParams {
+  void* out;
+  int out_f32;
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* cu_q_lens;
+  int B, Hq, Hkv, max_blocks, num_blocks, tiles_max;
+  float scale_log2;   // |scale| * log2(e)
+  uint32_t q_sign;    // 0x80008000 when scale < 0 (q is negated), else 0
+};
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Registers of one thread's share of a K/V tile: keys 2*kp and 2*kp+1 of the
+// tile, head_dim chunk [8c, 8c+8) (thread t: kp = t / 8, c = t % 8).
+struct TileRegs {
+  u32x4 k0, k1, v0, v1;
+};
+
+__device__ __forceinline__ void load_tile(TileRegs& r, const PParams& p, const int32_t* trow,
+                                          int g, int ctx, int k0, int tid) {
+  const int kp = tid >> 3, c = tid & 7;
+  const int key0 = k0 + 2 * kp, key1 = key0 + 1;
+  const u32x4 zero = {0, 0, 0, 0};
+  r.k0 = r.k1 = r.v0 = r.v1 = zero;
+  // a thread's two keys are in the same 16-token block (2*kp is even)
+  if (key0 < ctx) {
+    const int phys = trow[key0 / kBS];
+    if (phys >= 0 && phys < p.num_blocks) {
+      const int64_t base = (((int64_t)phys * p.Hkv + g) * kBS + (key0 % kBS)) * kD + 8 * c;
+      r.k0 = *reinterpret_cast<const u32x4*>(p.k_cache + base);
+      r.v0 = *reinterpret_cast<const u32x4*>(p.v_cache + base);
+      if (key1 < ctx) {
+        r.k1 = *reinterpret_cast<const u32x4*>(p.k_cache + base + kD);
+        r.v1 = *reinterpret_cast<const u32x4*>(p.v_cache + base + kD);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* ks, uint16_t* vt,
+                                           int tid) {
+  const int kp = tid >> 3, c = tid & 7;
+  *reinterpret_cast<u32x4*>(ks + (2 * kp) * kKRow + 8 * c) = r.k0;
+  *reinterpret_cast<u32x4*>(ks + (2 * kp + 1) * kKRow + 8 * c) = r.k1;
+  // V^T[d][key]: pair keys (2kp, 2kp+1) at each d into one dword
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t lo = __builtin_amdgcn_perm(r.v1[w], r.v0[w], 0x05040100u);  // d = 8c+2w
+    const uint32_t hi = __builtin_amdgcn_perm(r.v1[w], r.v0[w], 0x07060302u);  // d = 8c+2w+1
+    *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * w) * kVRow + 2 * kp) = lo;
+    *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * w + 1) * kVRow + 2 * kp) = hi;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+prefill_kernel(PParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks_buf[2][kTile * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_buf[2][kD * kVRow];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // grid: g fastest, then b, then query tile from the last (heaviest) down
+  const int g = blockIdx.x % p.Hkv;
+  const int rest = blockIdx.x / p.Hkv;
+  const int b = rest % p.B;
+  const int tile = p.tiles_max - 1 - rest / p.B;
+
+  const int qs = p.cu_q_lens[b];
+  const int q_len = p.cu_q_lens[b + 1] - qs;
+  const int q0 = tile * kTile;
+  if (q0 >= q_len) return;
+  int ctx = p.context_lens[b];
+  const int cap = p.max_blocks * kBS;
+  ctx = ctx > cap ? cap : ctx;
+  const int hist = ctx - q_len;  // position of query row 0 minus 0
+  const int rows = q_len - q0 < kTile ? q_len - q0 : kTile;
+  const int pos_first = hist + q0;
+  const int pos_last = hist + q0 + rows - 1;
+  int kend = pos_last + 1 < ctx ? pos_last + 1 : ctx;  // keys [0, kend)
+  if (kend < 0) kend = 0;
+  const int n_tiles = (kend + kTile - 1) / kTile;
+  const int h = 4 * g + wave;
+  const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks;
+
+  // Q^T operand: lane holds q row (qt*32 + lane%32), d in [ks*16 + 8*(lane/32), +8)
+  const int lr = lane & 31, lh = lane >> 5;
+  bf16x8_t qop[2][4];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    int row = q0 + qt * 32 + lr;
+    row = row < q_len ? row : q_len - 1;
+    const uint16_t* qr = p.q + ((int64_t)(qs + row) * p.Hq + h) * kD + 8 * lh;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qr + 16 * k);
+      v ^= u32x4{p.q_sign, p.q_sign, p.q_sign, p.q_sign};
+      qop[qt][k] = as_bf16x8(v);
+    }
+  }
+
+  f32x16 o[2][2];  // [dt][qt]
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[a][c][r] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+
+  TileRegs nxt;
+  if (n_tiles > 0) {
+    load_tile(nxt, p, trow, g, ctx, 0, tid);
+    store_tile(nxt, ks_buf[0], vt_buf[0], tid);
+  }
+  __syncthreads();
+
+  for (int it = 0; it < n_tiles; ++it) {
+    const int k0 = it * kTile;
+    const int buf = it & 1;
+    if (it + 1 < n_tiles) load_tile(nxt, p, trow, g, ctx, k0 + kTile, tid);
+    const uint16_t* ks = ks_buf[buf];
+    const uint16_t* vt = vt_buf[buf];
+
+    // S^T = K . Q^T  (scores before scaling)
+    f32x16 s[2][2];  // [kt][qt]
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][qt][r] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const bf16x8_t a = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(ks + (kt * 32 + lr) * kKRow + 16 * k + 8 * lh));
+        s[kt][0] = mfma(a, qop[0][k], s[kt][0]);
+        s[kt][1] = mfma(a, qop[1][k], s[kt][1]);
+      }
+    }
+
+    // causal mask on tiles that reach past the first row's position
+    if (k0 + kTile - 1 > pos_first) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const int pos = pos_first + qt * 32 + lr;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+            if (key > pos || key >= ctx) s[kt][qt][r] = -INFINITY;
+          }
+        }
+    }
+
+    // online softmax per query column (lane%32 of each qt), log2 domain
+    bf16x8_t pop[2][4];  // P^T operand [qt][key step]
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float mx = s[0][qt][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][qt][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][qt][r]);
+      mx = fmaxf(mx, shfl_xor(mx, 32)) * p.scale_log2;
+      const float m_new = fmaxf(m_run[qt], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_use);
+      m_run[qt] = m_new;
+      l_run[qt] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][qt][r] *= alpha;
+      float lsum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        float pr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          pr[r] = __builtin_amdgcn_exp2f(s[kt][qt][r] * p.scale_log2 - m_use);
+          lsum += pr[r];
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          u32x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = pack_bf16(pr[8 * half + 2 * e], pr[8 * half + 2 * e + 1]);
+          pop[qt][2 * kt + half] = as_bf16x8(w);
+        }
+      }
+      l_run[qt] += lsum;
+    }
+
+    // O^T += V^T . P^T
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kb = st * 16;  // key offset of this 16-key step within the tile
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const uint16_t* vrow = vt + (dt * 32 + lr) * kVRow + kb + 4 * lh;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+        const bf16x8_t a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        o[dt][0] = mfma(a, pop[0][st], o[dt][0]);
+        o[dt][1] = mfma(a, pop[1][st], o[dt][1]);
+      }
+    }
+
+    if (it + 1 < n_tiles) store_tile(nxt, ks_buf[buf ^ 1], vt_buf[buf ^ 1], tid);
+    __syncthreads();
+  }
+
+  // epilogue: out[row][h][d] = O^T[d][row] / l(row)
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float lt = l_run[qt] + shfl_xor(l_run[qt], 32);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    const int row = q0 + qt * 32 + lr;
+    if (row >= q_len) continue;
+    const int64_t base = ((int64_t)(qs + row) * p.Hq + h) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int d = dt * 32 + 8 * gq + 4 * lh;
+        const float x0 = o[dt][qt][4 * gq + 0] * inv, x1 = o[dt][qt][4 * gq + 1] * inv;
+        const float x2 = o[dt][qt][4 * gq + 2] * inv, x3 = o[dt][qt][4 * gq + 3] * inv;
+        if (p.out_f32) {
+          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + base + d) =
+              make_float4(x0, x1, x2, x3);
+        } else {
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + base + d) =
+              u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
+        }
+      }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  PParams p;
+  p.out = a.out;
+  p.out_f32 = a.out_f32;
+  p.q = (const uint16_t*)a.q;
+  p.k_cache = (const uint16_t*)a.k_cache;
+  p.v_cache = (const uint16_t*)a.v_cache;
+  p.block_tables = a.block_tables;
+  p.context_lens = a.context_lens;
+  p.cu_q_lens = a.cu_q_lens;
+  p.B = a.B;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.max_blocks = a.max_blocks_per_seq;
+  p.num_blocks = a.num_blocks;
+  p.tiles_max = (a.max_q_len + kTile - 1) / kTile;
+  // |scale| in log2 units, floored so that a zero scale still maps masked
+  // (-inf) scores to -inf instead of NaN; any real score times 1e-30 is 0.
+  p.scale_log2 = (a.scale < 0.f ? -a.scale : a.scale) * kLog2e;
+  if (p.scale_log2 < 1e-30f) p.scale_log2 = 1e-30f;
+  p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
+  const int64_t grid = (int64_t)p.tiles_max * a.B * a.Hkv;
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
 
 }  // namespace pkv
