@@ -130,8 +130,12 @@ PKV_API size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int3
  *               across shares are merged the same way.
  * workspace     device scratch of at least
  *               paged_attention_decode_workspace_size(...) bytes (may be NULL
- *               when that is 0).  Its contents need no initialisation and
- *               are meaningless after the call.
+ *               when that is 0).  It must be zero-filled before its first use;
+ *               its first 128 KiB hold per-stream split counters that every
+ *               call leaves at zero again, so one zero-fill serves all later
+ *               calls, whatever their shapes.  Calls that share a workspace
+ *               must not run concurrently (they would race on it).  Splits
+ *               handle up to 32768 (sequence, KV head) streams.
  * This build implements D == 64, block_size == 16 and Hq == 4 * Hkv
  * (PKV_ERR_UNSUPPORTED otherwise).  Empty contexts give zero rows.
  */

@@ -183,9 +183,10 @@ def paged_attention_prefill_causal(out, q, k_cache, v_cache, block_tables, conte
 
 
 def decode_workspace(B, Hq, Hkv, D, block_size, max_context_len, partition_size, device):
-    """Allocate (with torch) the workspace a decode call needs, or None."""
+    """Allocate (with torch) the zero-filled workspace a decode call needs, or
+    None.  Later calls leave it zeroed, so it can be reused call after call."""
     n = paged_attention_decode_workspace_size(B, Hq, Hkv, D, block_size, max_context_len,
                                               partition_size)
     if n == 0:
         return None
-    return _torch().empty(n, dtype=_torch().uint8, device=device)
+    return _torch().zeros(n, dtype=_torch().uint8, device=device)

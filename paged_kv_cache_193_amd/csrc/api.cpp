@@ -74,8 +74,14 @@ int plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_siz
                 partition_size);
   }
   plan->records = pkv::decode_records(plan->mode, B, Hkv, plan->parts_max);
-  plan->bytes = plan->records * (pkv::kRecordFloats + 8) * sizeof(float);
-  if (plan->mode == pkv::kAuto) plan->bytes += (size_t)(B + 2) * sizeof(int32_t);
+  plan->bytes = 0;
+  if (plan->records) {
+    if ((int64_t)B * Hkv > pkv::kMaxSplitStreams)
+      return fail(PKV_ERR_UNSUPPORTED, "split decode handles B*Hkv <= %d streams (got %lld)",
+                  pkv::kMaxSplitStreams, (long long)B * Hkv);
+    // counter region, then records (normalised outputs) and their (m, l) pairs
+    plan->bytes = pkv::kCounterBytes + plan->records * (pkv::kRecordFloats + 8) * sizeof(float);
+  }
   return PKV_OK;
 }
 
@@ -146,7 +152,6 @@ int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const vo
   }
   if ((int64_t)B * Hkv * plan.parts_max / 4 >= INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "too many (sequence, head, partition) units for one launch");
-  float* ws = static_cast<float*>(workspace);
   pkv::DecodeArgs a;
   a.out = out;
   a.out_f32 = out_dtype == PKV_OUT_F32;
@@ -165,8 +170,12 @@ int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const vo
   a.mode = plan.mode;
   a.part_blocks = plan.part_blocks;
   a.parts_max = plan.parts_max;
-  a.ws_o = plan.bytes ? ws : nullptr;
-  a.ws_ml = plan.bytes ? ws + plan.records * pkv::kRecordFloats : nullptr;
+  float* rec = plan.bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                     pkv::kCounterBytes)
+                         : nullptr;
+  a.ws_count = plan.bytes ? static_cast<uint32_t*>(workspace) : nullptr;
+  a.ws_o = rec;
+  a.ws_ml = plan.bytes ? rec + plan.records * pkv::kRecordFloats : nullptr;
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream), "paged_attention_decode launch");
 }
 

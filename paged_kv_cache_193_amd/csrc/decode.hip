@@ -35,8 +35,10 @@
 // P.V is again v_dot2_f32_bf16 with an fp32 accumulator.
 //
 // Split contexts: a segment that does not cover its whole stream writes a
-// partial record (normalised output, m, l) and decode_merge_kernel combines
-// the records of a stream by log-sum-exp.
+// partial record (normalised output, m, l) to the workspace and counts it on
+// a per-stream counter; the wavefront that writes the stream's last piece
+// merges all pieces by log-sum-exp (no second kernel) and re-zeroes the
+// counter.
 #include "device_common.h"
 #include "launch.h"
 
@@ -75,7 +77,14 @@ struct Params {
   int part_blocks, parts_max;
   float* ws_o;
   float* ws_ml;
-  int* ws_pfx;  // auto mode: per-sequence block prefix, then NB and the chunk size
+  uint32_t* ws_count;  // per stream (b, g): split records written so far
+};
+
+// Where the split records of one stream live: piece k of the stream is
+// record base + k * stride (+ first_extra for k == 0).
+struct RecordList {
+  int64_t base;
+  int stride, first_extra, pieces;
 };
 
 __device__ __forceinline__ int eff_ctx(const Params& p, int b) {
@@ -274,8 +283,8 @@ __device__ __forceinline__ void run_segment(LaneState& st, const Params& p, int 
 // Combine the 64 lanes' states of a finished segment and write either the
 // final rows out[b][4g..4g+3][:] or a split record.  red: this wave's 8 KB.
 __device__ __forceinline__ void finish_segment(const LaneState& st, const Params& p, int b,
-                                               int g, bool complete, int record, float* red,
-                                               int lane) {
+                                               int g, bool complete, int record,
+                                               const RecordList& rl, float* red, int lane) {
   const int grp = lane >> 3, i = lane & 7;
   const bool quad1 = (i & 4) != 0;
   const int c = quad1 ? ((i & 3) ^ 3) : (i & 3);
@@ -336,13 +345,88 @@ __device__ __forceinline__ void finish_segment(const LaneState& st, const Params
       u32x2 pk = {pack_bf16(o.x, o.y), pack_bf16(o.z, o.w)};
       *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + row) = pk;
     }
-  } else {
-    *reinterpret_cast<float4*>(p.ws_o + (int64_t)record * kRecordFloats + h * kD + d4) = o;
-    if ((lane & 15) == 0) {
-      p.ws_ml[((int64_t)record * 4 + h) * 2 + 0] = m_h;
-      p.ws_ml[((int64_t)record * 4 + h) * 2 + 1] = l_h;
+    return;
+  }
+  // Split stream: write this piece's record with agent-scope (sc1) stores;
+  // publish_piece() counts it once the stores have completed.
+  float* ro = p.ws_o + (int64_t)record * kRecordFloats + h * kD + d4;
+  __hip_atomic_store(ro + 0, o.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(ro + 1, o.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(ro + 2, o.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(ro + 3, o.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((lane & 15) == 0) {
+    float* rml = p.ws_ml + ((int64_t)record * 4 + h) * 2;
+    __hip_atomic_store(rml + 0, m_h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(rml + 1, l_h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Wait until every store this wavefront issued has completed (vmcnt 0).  The
+// signal fences keep the compiler from moving memory operations across it.
+__device__ __forceinline__ void drain_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Count one stored piece of stream (b, g) (its record stores must have
+// completed: drain_stores()).  The wavefront that completes the count merges
+// all pieces by log-sum-exp and re-zeroes the counter.  Records are read with
+// agent-scope (sc1) loads and the counter is an agent-scope atomic, so pieces
+// written on other XCDs are seen without any cache flush.
+__device__ __forceinline__ void publish_piece(const Params& p, int b, int g,
+                                              const RecordList& rl, int lane) {
+  const int h = lane >> 4;
+  const int d4 = (lane & 15) * 4;
+  uint32_t* cnt = p.ws_count + (int64_t)b * p.Hkv + g;
+  uint32_t before = 0;
+  if (lane == 0) before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  before = __builtin_amdgcn_readfirstlane(before);
+  if (before + 1 != (uint32_t)rl.pieces) return;
+
+  // last piece in: merge all pieces of the stream, 8 pieces per round so their
+  // loads are in flight together
+  constexpr int kBatch = 8;
+  float M = -INFINITY, den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = 0; k0 < rl.pieces; k0 += kBatch) {
+    float bm[kBatch], bl[kBatch];
+    float4 bo[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int k = k0 + u < rl.pieces ? k0 + u : rl.pieces - 1;  // repeats are skipped below
+      const int64_t r = rl.base + (int64_t)k * rl.stride + (k == 0 ? rl.first_extra : 0);
+      const float* pml = p.ws_ml + (r * 4 + h) * 2;
+      const float* po = p.ws_o + r * kRecordFloats + h * kD + d4;
+      bm[u] = __hip_atomic_load(pml + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bl[u] = __hip_atomic_load(pml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bo[u].x = __hip_atomic_load(po + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bo[u].y = __hip_atomic_load(po + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bo[u].z = __hip_atomic_load(po + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bo[u].w = __hip_atomic_load(po + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (k0 + u >= rl.pieces || !(bl[u] > 0.f)) continue;
+      const float Mn = fmaxf(M, bm[u]);
+      const float a = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+      const float wk = bl[u] * __builtin_amdgcn_exp2f(bm[u] - Mn);
+      num = make_float4(num.x * a + wk * bo[u].x, num.y * a + wk * bo[u].y,
+                        num.z * a + wk * bo[u].z, num.w * a + wk * bo[u].w);
+      den = den * a + wk;
+      M = Mn;
     }
   }
+  const float inv2 = den > 0.f ? 1.0f / den : 0.f;
+  const float4 res = make_float4(num.x * inv2, num.y * inv2, num.z * inv2, num.w * inv2);
+  const int64_t row = ((int64_t)b * p.Hq + 4 * g + h) * kD + d4;
+  if (p.out_f32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row) = res;
+  } else {
+    u32x2 pk = {pack_bf16(res.x, res.y), pack_bf16(res.z, res.w)};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + row) = pk;
+  }
+  if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void write_zero_rows(const Params& p, int b, int g, int lane) {
@@ -383,165 +467,340 @@ decode_units_kernel(Params p) {
   LaneState st;
   run_segment(st, p, b, g, j0, j1, ctx, lane);
   const bool complete = (j0 == 0 && j1 == nb);
-  finish_segment(st, p, b, g, complete, unit, red[wave], lane);
+  RecordList rl;
+  rl.base = (int64_t)stream * parts;
+  rl.stride = 1;
+  rl.first_extra = 0;
+  rl.pieces = (nb + p.part_blocks - 1) / (p.part_blocks > 0 ? p.part_blocks : 1);
+  finish_segment(st, p, b, g, complete, unit, rl, red[wave], lane);
+  if (!complete) {
+    drain_stores();
+    publish_piece(p, b, g, rl, lane);
+  }
 }
 
-// kAuto: a fixed grid of kAutoWaves wavefronts; all blocks of all streams,
-// in (b, g) order, are cut into equal consecutive shares, one per wavefront.
-// A share covers at most two partial streams (its first and last segment);
-// every stream strictly inside a share is complete.  Record slots: wavefront
-// w owns records 2w (its first segment) and 2w+1 (its last).
+// ---------------------------------------------------------------------------
+// kAuto: balanced split over a fixed grid of kAutoWaves wavefronts.
+//
+// Every stream (b, g) is padded to a multiple of kRing blocks and all streams,
+// in (b, g) order, form one global block list whose ring groups are dealt out
+// as evenly as possible (shares differ by at most one group), one share per
+// wavefront.  So every ring group of kRing
+// blocks lies inside one stream, padding blocks are masked (their loads re-read
+// a real block of the stream), and a wavefront streams its share through ONE
+// continuous ring across stream boundaries: the next group's block ids (scalar
+// loads) and query rows (vector loads) are fetched one group ahead, so a new
+// stream costs no pipeline drain.  A share holds at most two partial streams
+// (its first and last segment); streams strictly inside it are complete and
+// written directly.  Record slots: wavefront w owns records 2w (first segment)
+// and 2w+1 (last segment).
+
+// First block of wavefront w's share when gbase groups go to every
+// wavefront and one more to the first `rem`.
+__device__ __forceinline__ int64_t share_start(int64_t w, int64_t gbase, int64_t rem) {
+  return (int64_t)kRing * (w * gbase + (w < rem ? w : rem));
+}
+
+// Wavefront whose share holds block x.
+__device__ __forceinline__ int64_t share_of(int64_t x, int64_t gbase, int64_t rem) {
+  const int64_t gx = x / kRing;
+  const int64_t big = rem * (gbase + 1);
+  if (gx < big) return gx / (gbase + 1);
+  return rem + (gx - big) / gbase;
+}
+
+__device__ __forceinline__ int padded_blocks(int ctx) {
+  const int nb = (ctx + kBS - 1) / kBS;
+  return (nb + kRing - 1) / kRing * kRing;
+}
+
+// Position in the padded block list; every field is wave-uniform.
+struct Cursor {
+  int b, g, j;      // stream (b, g), block j of it (a multiple of kRing)
+  int nbp, nbr;     // padded and real block counts of the stream
+  int ctx;          // context length of sequence b
+};
+
+__device__ __forceinline__ void cursor_load_seq(Cursor& c, const int* s_ctx, int b) {
+  c.b = b;
+  c.ctx = __builtin_amdgcn_readfirstlane(s_ctx[b]);
+  c.nbr = (c.ctx + kBS - 1) / kBS;
+  c.nbp = (c.nbr + kRing - 1) / kRing * kRing;
+}
+
+// Move one ring group forward (only called while the target is inside the
+// list, so b stays below B).
+__device__ __forceinline__ void cursor_advance(Cursor& c, const int* s_ctx, int Hkv, int B) {
+  c.j += kRing;
+  if (c.j < c.nbp) return;
+  c.j = 0;
+  if (++c.g < Hkv) return;
+  c.g = 0;
+  int b = c.b + 1;
+  while (b < B - 1 && __builtin_amdgcn_readfirstlane(s_ctx[b]) == 0) ++b;
+  cursor_load_seq(c, s_ctx, b);
+}
+
+// Block-id window: lane k returns the physical id of block xs + k of the
+// padded list (the cursor c sits at xs), clamped to its stream's last real
+// block; 0 past x1.  One vector load per 64 blocks; ids are then read with
+// readlane, so no scalar-load wait ever sits between two ring groups.
+__device__ __forceinline__ int id_window(const Params& p, const int* s_ctx, const Cursor& c,
+                                         int64_t xs, int64_t x1, int lane) {
+  if (xs + lane >= x1) return 0;
+  int b = c.b, g = c.g, j = c.j, nbp = c.nbp, nbr = c.nbr;
+  int k = lane;
+  while (k >= nbp - j) {
+    k -= nbp - j;
+    j = 0;
+    if (++g == p.Hkv) {
+      g = 0;
+      do {
+        ++b;
+      } while (b < p.B - 1 && s_ctx[b] == 0);
+      nbr = (s_ctx[b] + kBS - 1) / kBS;
+      nbp = (nbr + kRing - 1) / kRing * kRing;
+    }
+  }
+  j += k;
+  const int jj = j < nbr - 1 ? j : nbr - 1;
+  return p.block_tables[(int64_t)b * p.max_blocks + jj];
+}
+
+__device__ __forceinline__ void load_q(uint32_t (&qv)[4][4], const Params& p, int b, int g,
+                                       int i, int c) {
+  const uint16_t* qb = p.q + ((int64_t)b * p.Hq + 4 * g) * kD + 8 * i;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u32x4 v = *reinterpret_cast<const u32x4*>(qb + (j ^ c) * kD);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) qv[j][w] = v[w];
+  }
+}
+
+__device__ __forceinline__ void reset_state(LaneState& st) {
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.acc[j][e] = 0.f;
+}
+
 __global__ void __launch_bounds__(kWaves * 64)
 decode_auto_kernel(Params p) {
   __shared__ float red[kWaves][8 * 4 * kD];
   __shared__ int pfx[kAutoMaxBatch + 1];
-  __shared__ int part_sums[kWaves * 64];
+  __shared__ int s_ctx[kAutoMaxBatch];
+  __shared__ int wsum[kWaves];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // per-sequence block counts -> exclusive prefix in LDS
+  // per-sequence padded block counts -> exclusive prefix in LDS
   const int per = (p.B + kWaves * 64 - 1) / (kWaves * 64);
   const int beg = tid * per;
   const int end = beg + per < p.B ? beg + per : p.B;
   int local = 0;
-  for (int k = beg; k < end; ++k) local += (eff_ctx(p, k) + kBS - 1) / kBS;
-  part_sums[tid] = local;
-  __syncthreads();
-  for (int off = 1; off < kWaves * 64; off <<= 1) {
-    int v = tid >= off ? part_sums[tid - off] : 0;
-    __syncthreads();
-    part_sums[tid] += v;
-    __syncthreads();
+  for (int k = beg; k < end; ++k) {
+    const int c = eff_ctx(p, k);
+    s_ctx[k] = c;
+    local += padded_blocks(c);
   }
-  int run = tid ? part_sums[tid - 1] : 0;
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - local;
+  for (int w2 = 0; w2 < wave; ++w2) run += wsum[w2];
   for (int k = beg; k < end; ++k) {
     pfx[k] = run;
-    run += (eff_ctx(p, k) + kBS - 1) / kBS;
+    run += padded_blocks(s_ctx[k]);
   }
-  if (tid == kWaves * 64 - 1) pfx[p.B] = part_sums[tid];
+  if (tid == kWaves * 64 - 1) pfx[p.B] = run;
   __syncthreads();
 
+  // ring groups are dealt out as evenly as possible: the first `rem`
+  // wavefronts take gbase + 1 groups, the others gbase
   const int64_t NB = (int64_t)p.Hkv * __builtin_amdgcn_readfirstlane(pfx[p.B]);
   const int W = gridDim.x * kWaves;
-  const int64_t C = (NB + W - 1) / W;
-  if (blockIdx.x == 0) {  // publish the layout for the merge kernel
-    for (int k = tid; k <= p.B; k += kWaves * 64) p.ws_pfx[k] = pfx[k];
-    if (tid == 0) p.ws_pfx[p.B + 1] = (int)C;
+  const int64_t G = NB / kRing;
+  const int64_t gbase = G / W;
+  const int64_t rem = G - gbase * W;
+  // empty sequences have no blocks, so no wavefront meets them: workgroup
+  // k % grid writes their zero rows
+  for (int k = blockIdx.x; k < p.B; k += gridDim.x) {
+    if (s_ctx[k] == 0) {
+      for (int e = tid; e < p.Hq * kD; e += kWaves * 64) {
+        const int64_t idx = (int64_t)k * p.Hq * kD + e;
+        if (p.out_f32) reinterpret_cast<float*>(p.out)[idx] = 0.f;
+        else reinterpret_cast<uint16_t*>(p.out)[idx] = 0;
+      }
+    }
   }
   const int w = blockIdx.x * kWaves + wave;
-  int64_t x = (int64_t)w * C;
-  const int64_t x1 = x + C < NB ? x + C : NB;
-  const int64_t x0 = x;
-  while (x < x1) {
-    // sequence containing global block x: largest b with Hkv*pfx[b] <= x
-    int lo = 0, hi = p.B;
-    while (hi - lo > 1) {
-      int mid = (lo + hi) >> 1;
-      if ((int64_t)p.Hkv * pfx[mid] <= x) lo = mid; else hi = mid;
-    }
-    // values read from LDS are wave-uniform here; keep them in SGPRs
-    const int b = __builtin_amdgcn_readfirstlane(lo);
-    const int pb = __builtin_amdgcn_readfirstlane(pfx[b]);
-    const int nb = __builtin_amdgcn_readfirstlane(pfx[b + 1]) - pb;
-    const int64_t off = x - (int64_t)p.Hkv * pb;
-    const int g = (int)(off / nb);
-    const int jb = (int)(off - (int64_t)g * nb);
-    const int64_t stream_end = x - jb + nb;
-    const int64_t xe = x1 < stream_end ? x1 : stream_end;
-    const int je = jb + (int)(xe - x);
-    LaneState st;
-    run_segment(st, p, b, g, jb, je, eff_ctx(p, b), lane);
-    const bool complete = (jb == 0 && je == nb);
-    const int64_t stream_start = x - jb;
-    const int record = 2 * w + (stream_start <= x0 ? 0 : 1);
-    finish_segment(st, p, b, g, complete, record, red[wave], lane);
-    x = xe;
+  const int64_t x0 = share_start(w, gbase, rem);
+  const int64_t x1 = share_start(w + 1, gbase, rem);
+  if (x0 >= x1) return;
+
+  const int grp = lane >> 3, i = lane & 7;
+  const bool quad1 = (i & 4) != 0;
+  const int c = quad1 ? ((i & 3) ^ 3) : (i & 3);
+  const int own_tok = quad1 ? grp + 8 : grp;
+  const int lane_off = grp * kD + 8 * i;
+
+  // locate x0: largest b with Hkv * pfx[b] <= x0
+  int lo = 0, hi = p.B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)p.Hkv * pfx[mid] <= x0) lo = mid; else hi = mid;
   }
-}
+  Cursor cc;
+  cursor_load_seq(cc, s_ctx, __builtin_amdgcn_readfirstlane(lo));
+  {
+    const int64_t off = x0 - (int64_t)p.Hkv * __builtin_amdgcn_readfirstlane(pfx[cc.b]);
+    cc.g = (int)(off / cc.nbp);
+    cc.j = (int)(off - (int64_t)cc.g * cc.nbp);
+  }
 
-// Log-sum-exp merge of split records, one workgroup per stream (b, g).
-// The (m, l) pairs of up to kMergeChunk records x 4 heads are staged in LDS
-// with one parallel load; then thread (head h = tid / 64, d = tid % 64)
-// folds the chunk into its running (M, numerator, denominator) with
-// independent loads of the records' outputs.
-constexpr int kMergeChunk = 256;
-
-template <int kMode>
-__global__ void __launch_bounds__(256)
-decode_merge_kernel(Params p) {
-  __shared__ float sm[kMergeChunk][4];
-  __shared__ float sl[kMergeChunk][4];
-  __shared__ int64_t srec[kMergeChunk];
-  const int stream = blockIdx.x;
-  const int b = stream / p.Hkv;
-  const int g = stream - b * p.Hkv;
-  const int tid = threadIdx.x;
-  const int h = tid >> 6;
-  const int d = tid & 63;
-  int count, first = 0, w0 = 0;
-  int64_t start_x = 0, C = 1;
-  if (kMode == kFixed) {
-    const int ctx = eff_ctx(p, b);
-    const int nb = (ctx + kBS - 1) / kBS;
-    count = (nb + p.part_blocks - 1) / p.part_blocks;
-    first = stream * p.parts_max;
+  // prologue: id window and q of the first group, then issue it
+  Cursor ci = cc;
+  int64_t xi = x0;
+  int64_t win = x0;
+  int tab = id_window(p, s_ctx, ci, x0, x1, lane);
+  BlockRegs ring[kRing];
+  int nvalid[kRing];
+  uint32_t qv[4][4], qn[4][4];
+  load_q(qn, p, ci.b, ci.g, i, c);
+#pragma unroll
+  for (int s = 0; s < kRing; ++s) {
+    const int j = ci.j + s < ci.nbr - 1 ? ci.j + s : ci.nbr - 1;
+    const int id = __builtin_amdgcn_readlane(tab, (int)(xi - win) + s);
+    const int nv = issue_block(ring[s], p, id, ci.g, j, ci.ctx, lane_off);
+    nvalid[s] = ci.j + s < ci.nbr ? nv : 0;
+  }
+  if (xi + kRing < x1) {
+    xi += kRing;
+    cursor_advance(ci, s_ctx, p.Hkv, p.B);
   } else {
-    const int pb = p.ws_pfx[b], nb = p.ws_pfx[b + 1] - pb;
-    if (nb == 0) {  // empty context: zero rows (no wavefront saw this stream)
-      if (tid < 64) write_zero_rows(p, b, g, tid);
-      return;
-    }
-    C = p.ws_pfx[p.B + 1];
-    start_x = (int64_t)p.Hkv * pb + (int64_t)g * nb;
-    w0 = (int)(start_x / C);
-    const int w1 = (int)((start_x + nb - 1) / C);
-    count = w1 - w0 + 1;
+    xi = x1;  // nothing left to issue: further refills re-read this group
   }
-  if (count <= 1) return;  // written directly by the decode kernel
+  // refills re-read the last issued group once the share is used up
+  int64_t xr = xi < x1 ? xi : xi - kRing;
+  if (xr - win + kRing > 64) {
+    win = xr;
+    tab = id_window(p, s_ctx, ci, xr, x1, lane);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+  }
 
-  float M = -INFINITY, num = 0.f, den = 0.f;
-  for (int k0 = 0; k0 < count; k0 += kMergeChunk) {
-    const int n = count - k0 < kMergeChunk ? count - k0 : kMergeChunk;
-    __syncthreads();
-    for (int idx = tid; idx < n * 4; idx += 256) {
-      const int k = idx >> 2, hh = idx & 3;
-      int64_t r;
-      if (kMode == kFixed) {
-        r = first + k0 + k;
-      } else {
-        const int w = w0 + k0 + k;
-        r = 2LL * w + ((k0 + k == 0 && start_x > (int64_t)w0 * C) ? 1 : 0);
+  // pieces of split streams this share holds (at most its first and last)
+  int pend = 0, pb0 = 0, pg0 = 0, pb1 = 0, pg1 = 0;
+  RecordList prl0 = {}, prl1 = {};
+
+  LaneState st;
+  reset_state(st);
+  int64_t seg_start = x0;  // where the current segment began in this share
+  for (int64_t xc = x0; xc < x1; xc += kRing) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) qv[j][w2] = qn[j][w2];
+
+    bool full = true;
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) full = full && nvalid[s] == kBS;
+    float x[kRing];
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+      x[s] = block_score(ring[s], qv, p.scale_log2, quad1);
+      if (!full && own_tok >= nvalid[s]) x[s] = -INFINITY;
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int s = 1; s < kRing; ++s) mx = fmaxf(mx, x[s]);
+    mx = fmaxf(mx, dpp<kRowHalfMirror>(mx));
+    const float m_new = fmaxf(st.m, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+    st.m = m_new;
+    st.l *= alpha;
+    const float a1 = dpp<kQuadXor1>(alpha), a2 = dpp<kQuadXor2>(alpha),
+                a3 = dpp<kQuadXor3>(alpha);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      st.acc[0][e] *= alpha;
+      st.acc[1][e] *= a1;
+      st.acc[2][e] *= a2;
+      st.acc[3][e] *= a3;
+    }
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+      const float pw = __builtin_amdgcn_exp2f(x[s] - m_use);
+      st.l += pw;
+      if (full)
+        block_pv<false>(st, ring[s], pw, quad1, true, true);
+      else
+        block_pv<true>(st, ring[s], pw, quad1, grp < nvalid[s], grp + 8 < nvalid[s]);
+      // refill the slot from the group at ci (a re-read when none is left)
+      const int j = ci.j + s < ci.nbr - 1 ? ci.j + s : ci.nbr - 1;
+      const int id = __builtin_amdgcn_readlane(tab, (int)(xr - win) + s);
+      const int nv = issue_block(ring[s], p, id, ci.g, j, ci.ctx, lane_off);
+      nvalid[s] = ci.j + s < ci.nbr ? nv : 0;
+      if (s == 0) load_q(qn, p, ci.b, ci.g, i, c);
+    }
+    if (xi + kRing < x1) {
+      xi += kRing;
+      cursor_advance(ci, s_ctx, p.Hkv, p.B);
+    } else {
+      xi = x1;
+    }
+    xr = xi < x1 ? xi : xi - kRing;
+    if (xr - win + kRing > 64) {
+      win = xr;
+      tab = id_window(p, s_ctx, ci, xr, x1, lane);
+      // wait here (vmcnt 0), inside the branch, so the common path carries
+      // no wait for this load
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+    }
+
+    // segment end: the stream ends here or the share does
+    const bool stream_ends = cc.j + kRing == cc.nbp;
+    if (stream_ends || xc + kRing >= x1) {
+      const int64_t stream_start =
+          (int64_t)p.Hkv * __builtin_amdgcn_readfirstlane(pfx[cc.b]) + (int64_t)cc.g * cc.nbp;
+      const bool complete = stream_ends && stream_start >= seg_start;
+      const int record = 2 * w + (stream_start <= x0 ? 0 : 1);
+      const int64_t w0 = share_of(stream_start, gbase, rem);
+      RecordList rl;
+      rl.base = 2 * w0;
+      rl.stride = 2;
+      rl.first_extra = stream_start > share_start(w0, gbase, rem) ? 1 : 0;
+      rl.pieces = (int)(share_of(stream_start + cc.nbp - 1, gbase, rem) - w0 + 1);
+      finish_segment(st, p, cc.b, cc.g, complete, record, rl, red[wave], lane);
+      if (!complete) {
+        if (pend == 0) {
+          pb0 = cc.b; pg0 = cc.g; prl0 = rl;
+        } else {
+          pb1 = cc.b; pg1 = cc.g; prl1 = rl;
+        }
+        ++pend;
       }
-      if (hh == 0) srec[k] = r;
-      sm[k][hh] = p.ws_ml[(r * 4 + hh) * 2 + 0];
-      sl[k][hh] = p.ws_ml[(r * 4 + hh) * 2 + 1];
+      reset_state(st);
+      seg_start = xc + kRing;
     }
-    __syncthreads();
-    float Mc = -INFINITY;
-    for (int k = 0; k < n; ++k)
-      if (sl[k][h] > 0.f) Mc = fmaxf(Mc, sm[k][h]);
-    if (Mc == -INFINITY) continue;
-    const float Mn = fmaxf(M, Mc);
-    const float rescale = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-    num *= rescale;
-    den *= rescale;
-    M = Mn;
-#pragma unroll 8
-    for (int k = 0; k < n; ++k) {
-      const float l = sl[k][h];
-      const float wgt = l > 0.f ? l * __builtin_amdgcn_exp2f(sm[k][h] - M) : 0.f;
-      const float o = p.ws_o[srec[k] * kRecordFloats + h * kD + d];
-      num += wgt * o;
-      den += wgt;
-    }
+    if (xc + kRing < x1) cursor_advance(cc, s_ctx, p.Hkv, p.B);
   }
-  const float o = den > 0.f ? num / den : 0.f;
-  const int64_t row = ((int64_t)b * p.Hq + 4 * g + h) * kD + d;
-  if (p.out_f32)
-    reinterpret_cast<float*>(p.out)[row] = o;
-  else
-    reinterpret_cast<uint16_t*>(p.out)[row] = to_bf16_bits(o);
+  // count this share's split pieces only now: one drain instead of one per
+  // segment in the middle of the stream
+  if (pend) {
+    drain_stores();
+    publish_piece(p, pb0, pg0, prl0, lane);
+    if (pend > 1) publish_piece(p, pb1, pg1, prl1, lane);
+  }
 }
 
 }  // namespace
@@ -573,9 +832,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.parts_max = a.parts_max;
   p.ws_o = a.ws_o;
   p.ws_ml = a.ws_ml;
-  p.ws_pfx = a.ws_o ? reinterpret_cast<int*>(
-                          a.ws_ml + decode_records(a.mode, a.B, a.Hkv, a.parts_max) * 8)
-                    : nullptr;
+  p.ws_count = a.ws_count;
   const int streams = a.B * a.Hkv;
   if (a.mode == kWhole) {
     const int grid = (streams + kWaves - 1) / kWaves;
@@ -584,12 +841,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     const int64_t units = (int64_t)streams * a.parts_max;
     const int grid = (int)((units + kWaves - 1) / kWaves);
     hipLaunchKernelGGL(decode_units_kernel<kFixed>, dim3(grid), dim3(kWaves * 64), 0, stream, p);
-    if (a.parts_max > 1)
-      hipLaunchKernelGGL(decode_merge_kernel<kFixed>, dim3(streams), dim3(256), 0, stream, p);
   } else {
     hipLaunchKernelGGL(decode_auto_kernel, dim3(kAutoWaves / kWaves), dim3(kWaves * 64), 0,
                        stream, p);
-    hipLaunchKernelGGL(decode_merge_kernel<kAuto>, dim3(streams), dim3(256), 0, stream, p);
   }
   return hipGetLastError();
 }

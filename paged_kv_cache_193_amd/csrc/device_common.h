@@ -51,6 +51,15 @@ __device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kCtrl, 0xf, 0xf, true);
 }
 
+// Wave-uniform read of an int32 array that no kernel of this launch writes
+// (block tables, lengths): through the constant address space, so the
+// compiler issues a scalar load even where the kernel also stores to global
+// memory.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* p, int64_t idx) {
+  return ((const_i32_ptr)p)[idx];
+}
+
 // Value of x held by lane (lane ^ mask) for any mask < 64 (ds_bpermute).
 __device__ __forceinline__ float shfl_xor(float x, int mask) {
   int lane = __lane_id();

@@ -35,6 +35,11 @@ constexpr int kAutoMaxBatch = 4096;
 // One split record: normalised partial output for the 4 query heads of a
 // KV group (4 x 64 fp32) followed, in a separate array, by (m, l) per head.
 constexpr int kRecordFloats = 4 * 64;
+// Split counters (one uint32 per (sequence, KV head) stream) occupy a fixed
+// region at the start of the workspace, whatever the call's shapes, so a
+// workspace zero-filled once stays valid for every later call.
+constexpr int kMaxSplitStreams = 32768;
+constexpr size_t kCounterBytes = (size_t)kMaxSplitStreams * 4;
 
 struct DecodeArgs {
   void* out;
@@ -51,6 +56,7 @@ struct DecodeArgs {
   int32_t parts_max;       // kFixed: partitions per stream upper bound
   float* ws_o;             // records x kRecordFloats
   float* ws_ml;            // records x 4 heads x (m, l)
+  uint32_t* ws_count;      // B x Hkv split counters, zero between calls
 };
 size_t decode_records(int32_t mode, int32_t B, int32_t Hkv, int32_t parts_max);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -167,3 +167,23 @@ def test_long_context_split_full_size():
     assert_close(auto.cpu().numpy(), ref, "long auto")
     del c
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("partition", [32, pkv.PARTITION_AUTO])
+def test_shared_workspace_reused_across_calls(partition):
+    """One workspace, many calls on different batches: each result matches the
+    oracle and the per-stream counters are back at zero after every call."""
+    cases = [ragged_case(67, [700, 33, 1, 928, 999]), ragged_case(68, [5, 1024, 64, 300]),
+             ragged_case(69, [1024, 1024, 17])]
+    refs = [oracle_decode(c) for c in cases]
+    ws = pkv.decode_workspace(5, 32, 8, 64, 16, 1024, partition, "cuda")
+    for rep in range(3):
+        for c, ref in zip(cases, refs):
+            out = torch.empty((c.B, c.Hq, c.D), dtype=torch.float32, device="cuda")
+            pkv.paged_attention_decode(out, dev(c.q), dev(c.k_cache), dev(c.v_cache),
+                                       dev(c.block_tables), dev(c.context_lens), c.scale, 1024,
+                                       partition, ws)
+            torch.cuda.synchronize()
+            assert_close(out.cpu().numpy(), ref, f"reuse p={partition} rep={rep} B={c.B}")
+            counters = ws[:32768 * 4].view(torch.int32)
+            assert int(counters.abs().sum()) == 0
