@@ -28,9 +28,10 @@
 // same register choice on every lane.
 //
 // Online softmax (fp32, log2 domain): the lane pair (i, 7-i) shares a running
-// max m for head c over its two token streams; the running max is only moved
-// when a score exceeds it by more than 2^8 (lazy rescale, exact by the
-// softmax shift identity; weights stay <= 2^8).  P.V packs the two tokens'
+// max m for head c over its two token streams; m moves once per group of
+// kRing blocks and the accumulator is rescaled then, without a branch (the
+// softmax shift identity makes the result independent of when m moves, up to
+// rounding).  P.V packs the two tokens'
 // weights as a bf16 pair and V into (token grp, token grp+8) pairs per d, so
 // P.V is again v_dot2_f32_bf16 with an fp32 accumulator.
 //
