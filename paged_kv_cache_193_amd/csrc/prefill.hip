@@ -45,6 +45,8 @@ constexpr int kBS = 16;
 constexpr int kTile = 64;          // query rows per workgroup and keys per K/V tile
 constexpr int kKRow = kD + 8;      // K tile row stride (bf16 elements): 144 bytes
 constexpr int kVRow = kTile + 4;   // V^T tile row stride (bf16 elements): 136 bytes
+constexpr float kLazyLog2 = 8.0f;  // the running max may lag the true max by 2^8
+constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 pair (1, 1)
 
 struct PParams {
   void* out;
@@ -60,6 +62,9 @@ struct PParams {
   uint32_t q_sign;    // 0x80008000 when scale < 0 (q is negated), else 0
 };
 
+constexpr f32x16 kZero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
+                             0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+
 __device__ __forceinline__ f32x16 mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -74,25 +79,33 @@ struct TileRegs {
   u32x4 k0, k1, v0, v1;
 };
 
-__device__ __forceinline__ void load_tile(TileRegs& r, const PParams& p, const int32_t* trow,
-                                          int g, int ctx, int k0, int tid) {
+// Physical id of the block holding this thread's keys in the tile that starts
+// at key k0 (the logical block index is clamped to the table row, so the read
+// is always in bounds; keys past the context are zeroed by load_tile).
+__device__ __forceinline__ int tile_block_id(const PParams& p, const int32_t* trow, int k0,
+                                             int tid) {
+  int jb = (k0 + 2 * (tid >> 3)) / kBS;
+  jb = jb < p.max_blocks ? jb : p.max_blocks - 1;
+  return trow[jb];
+}
+
+// Load this thread's share of the tile at key k0 from block `phys`.  The
+// loads are unconditional (an invalid id reads block 0), so the number of
+// loads in flight is the same on every path; rows of keys past the context
+// or of an invalid block are replaced by zeros afterwards.
+__device__ __forceinline__ void load_tile(TileRegs& r, const PParams& p, int phys, int g,
+                                          int ctx, int k0, int tid) {
   const int kp = tid >> 3, c = tid & 7;
-  const int key0 = k0 + 2 * kp, key1 = key0 + 1;
+  const int key0 = k0 + 2 * kp;  // key0 and key0 + 1 share one 16-token block
+  const bool ok = phys >= 0 && phys < p.num_blocks;
+  const int64_t base = (((int64_t)(ok ? phys : 0) * p.Hkv + g) * kBS + (key0 % kBS)) * kD + 8 * c;
+  r.k0 = *reinterpret_cast<const u32x4*>(p.k_cache + base);
+  r.v0 = *reinterpret_cast<const u32x4*>(p.v_cache + base);
+  r.k1 = *reinterpret_cast<const u32x4*>(p.k_cache + base + kD);
+  r.v1 = *reinterpret_cast<const u32x4*>(p.v_cache + base + kD);
   const u32x4 zero = {0, 0, 0, 0};
-  r.k0 = r.k1 = r.v0 = r.v1 = zero;
-  // a thread's two keys are in the same 16-token block (2*kp is even)
-  if (key0 < ctx) {
-    const int phys = trow[key0 / kBS];
-    if (phys >= 0 && phys < p.num_blocks) {
-      const int64_t base = (((int64_t)phys * p.Hkv + g) * kBS + (key0 % kBS)) * kD + 8 * c;
-      r.k0 = *reinterpret_cast<const u32x4*>(p.k_cache + base);
-      r.v0 = *reinterpret_cast<const u32x4*>(p.v_cache + base);
-      if (key1 < ctx) {
-        r.k1 = *reinterpret_cast<const u32x4*>(p.k_cache + base + kD);
-        r.v1 = *reinterpret_cast<const u32x4*>(p.v_cache + base + kD);
-      }
-    }
-  }
+  if (!(ok && key0 < ctx)) r.k0 = r.v0 = zero;
+  if (!(ok && key0 + 1 < ctx)) r.k1 = r.v1 = zero;
 }
 
 __device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* ks, uint16_t* vt,
@@ -110,7 +123,7 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* ks, uint
   }
 }
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 prefill_kernel(PParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t ks_buf[2][kTile * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t vt_buf[2][kD * kVRow];
@@ -167,89 +180,112 @@ prefill_kernel(PParams p) {
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
 
+  // K/V tiles go global -> registers -> LDS one tile ahead of the MFMAs, and
+  // the block id of the tile after that is read one more tile ahead, so no
+  // load waits on a table read.
   TileRegs nxt;
-  if (n_tiles > 0) {
-    load_tile(nxt, p, trow, g, ctx, 0, tid);
-    store_tile(nxt, ks_buf[0], vt_buf[0], tid);
-  }
+  int id_next = tile_block_id(p, trow, kTile, tid);
+  load_tile(nxt, p, tile_block_id(p, trow, 0, tid), g, ctx, 0, tid);
+  store_tile(nxt, ks_buf[0], vt_buf[0], tid);
   __syncthreads();
 
   for (int it = 0; it < n_tiles; ++it) {
     const int k0 = it * kTile;
     const int buf = it & 1;
-    if (it + 1 < n_tiles) load_tile(nxt, p, trow, g, ctx, k0 + kTile, tid);
+    // past the last tile these read clamped, unused data (no branch, so the
+    // load counts stay static)
+    load_tile(nxt, p, id_next, g, ctx, k0 + kTile, tid);
+    id_next = tile_block_id(p, trow, k0 + 2 * kTile, tid);
     const uint16_t* ks = ks_buf[buf];
     const uint16_t* vt = vt_buf[buf];
 
-    // S^T = K . Q^T  (scores before scaling)
+    // S^T = K . Q^T  (scores before scaling); the first k-step starts from 0
     f32x16 s[2][2];  // [kt][qt]
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][qt][r] = 0.f;
-#pragma unroll
       for (int k = 0; k < 4; ++k) {
         const bf16x8_t a = as_bf16x8(
             *reinterpret_cast<const u32x4*>(ks + (kt * 32 + lr) * kKRow + 16 * k + 8 * lh));
-        s[kt][0] = mfma(a, qop[0][k], s[kt][0]);
-        s[kt][1] = mfma(a, qop[1][k], s[kt][1]);
+        s[kt][0] = mfma(a, qop[0][k], k == 0 ? kZero16 : s[kt][0]);
+        s[kt][1] = mfma(a, qop[1][k], k == 0 ? kZero16 : s[kt][1]);
       }
     }
 
-    // causal mask on tiles that reach past the first row's position
+    // causal mask on tiles that reach past the first row's position: key j of
+    // this lane's column is visible iff j <= min(pos, ctx - 1)
     if (k0 + kTile - 1 > pos_first) {
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int qt = 0; qt < 2; ++qt) {
+        const int pos = pos_first + qt * 32 + lr;
+        const int lim = (pos < ctx - 1 ? pos : ctx - 1) - (k0 + 4 * lh);
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          const int pos = pos_first + qt * 32 + lr;
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kt * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
-            if (key > pos || key >= ctx) s[kt][qt][r] = -INFINITY;
-          }
-        }
+          for (int r = 0; r < 16; ++r)
+            if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kt][qt][r] = -INFINITY;
+      }
     }
 
-    // online softmax per query column (lane%32 of each qt), log2 domain
-    bf16x8_t pop[2][4];  // P^T operand [qt][key step]
+    // Online softmax per query column (lane%32 of each qt), log2 domain.  The
+    // running max m_run is moved only when a column's tile max exceeds it by
+    // more than kLazyLog2; otherwise weights are exp2(score - m_run) <= 2^8
+    // and the accumulator is left alone (same result by the softmax shift
+    // identity).  The decision is wave-uniform.
+    float mx[2];
+    bool move = false;
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
-      float mx = s[0][qt][0];
+      float v = fmaxf(s[0][qt][0], s[0][qt][1]);
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][qt][r]);
+      for (int r = 2; r < 16; ++r) v = fmaxf(v, s[0][qt][r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][qt][r]);
-      mx = fmaxf(mx, shfl_xor(mx, 32)) * p.scale_log2;
-      const float m_new = fmaxf(m_run[qt], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qt] - m_use);
-      m_run[qt] = m_new;
-      l_run[qt] *= alpha;
+      for (int r = 0; r < 16; ++r) v = fmaxf(v, s[1][qt][r]);
+      mx[qt] = fmaxf(v, shfl_xor(v, 32)) * p.scale_log2;
+      move = move || mx[qt] > m_run[qt] + kLazyLog2;
+    }
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
+      for (int qt = 0; qt < 2; ++qt) {
+        const float m_new = fmaxf(m_run[qt], mx[qt]);
+        // m_run = -inf: nothing accumulated yet, alpha = 0
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qt] - m_new);
+        m_run[qt] = m_new;
+        l_run[qt] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][qt][r] *= alpha;
-      float lsum = 0.f;
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][qt][r] *= alpha;
+      }
+    }
+
+    // P^T operand [qt][key step] as bf16; the row sums add the same rounded
+    // weights that P.V uses (v_dot2 against (1, 1))
+    bf16x8_t pop[2][4];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float m_use = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
+      float lsum0 = 0.f, lsum1 = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        float pr[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          pr[r] = __builtin_amdgcn_exp2f(s[kt][qt][r] * p.scale_log2 - m_use);
-          lsum += pr[r];
-        }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           u32x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = pack_bf16(pr[8 * half + 2 * e], pr[8 * half + 2 * e + 1]);
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * half + 2 * e;
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][r], p.scale_log2, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][r + 1], p.scale_log2, -m_use));
+            w[e] = pack_bf16(p0, p1);
+            if (e & 1)
+              lsum1 = dot2_bf16(w[e], kOnesBf16x2, lsum1);
+            else
+              lsum0 = dot2_bf16(w[e], kOnesBf16x2, lsum0);
+          }
           pop[qt][2 * kt + half] = as_bf16x8(w);
         }
       }
-      l_run[qt] += lsum;
+      l_run[qt] += lsum0 + lsum1;
     }
 
     // O^T += V^T . P^T
@@ -267,7 +303,7 @@ prefill_kernel(PParams p) {
       }
     }
 
-    if (it + 1 < n_tiles) store_tile(nxt, ks_buf[buf ^ 1], vt_buf[buf ^ 1], tid);
+    store_tile(nxt, ks_buf[buf ^ 1], vt_buf[buf ^ 1], tid);
     __syncthreads();
   }
 
