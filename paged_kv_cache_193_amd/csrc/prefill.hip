@@ -20,9 +20,18 @@
 //
 // LDS per workgroup, double buffered: K tile [64 keys][64 d] row major and
 // V^T tile [64 d][64 keys] (the B-side key index must run along registers,
-// so V is transposed once per tile here and read back 8 bytes at a time).
-// Rows are padded to spread LDS banks.  Tiles past the context are zero
-// filled (never read from the pools), so 0 * NaN cannot reach the MFMA.
+// so V is transposed once per tile here and read back 8 bytes at a time),
+// plus each wavefront's Q^T operand.  Rows are padded to spread LDS banks.
+// Rows of keys past the context, or of an invalid block, are zero filled, so
+// 0 * NaN cannot reach the MFMA.
+//
+// Softmax (fp32, log2 units): weights are exp2(c * s - m) against a reference
+// maximum m per query column.  m is not recomputed every tile: only when a
+// lane's sum of one tile's weights exceeds kLazyBound (a score rose well
+// above m) or the column has no reference yet is the tile's maximum taken,
+// the accumulator and row sum rescaled and the weights formed again.  By the
+// softmax shift identity the result does not depend on the reference used.
+// Row sums add the same bf16-rounded weights that P.V uses.
 //
 // Causal rule: query row t of a prompt of q_len tokens whose sequence holds
 // context_len tokens sits at position context_len - q_len + t and sees keys
@@ -45,7 +54,9 @@ constexpr int kBS = 16;
 constexpr int kTile = 64;          // query rows per workgroup and keys per K/V tile
 constexpr int kKRow = kD + 8;      // K tile row stride (bf16 elements): 144 bytes
 constexpr int kVRow = kTile + 4;   // V^T tile row stride (bf16 elements): 136 bytes
-constexpr float kLazyLog2 = 8.0f;  // the running max may lag the true max by 2^8
+// A lane's partial row sum of one tile's weights above this (or not a number)
+// sends the tile through the exact-max path.  Weights stay below 2^10.
+constexpr float kLazyBound = 1024.f;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 pair (1, 1)
 
 struct PParams {
@@ -58,8 +69,8 @@ struct PParams {
   const int32_t* context_lens;
   const int32_t* cu_q_lens;
   int B, Hq, Hkv, max_blocks, num_blocks, tiles_max;
-  float scale_log2;   // |scale| * log2(e)
-  uint32_t q_sign;    // 0x80008000 when scale < 0 (q is negated), else 0
+  float c_log2;     // |scale| * log2(e), floored at 1e-30: scores to log2 units
+  uint32_t q_sign;  // 0x80008000 when scale < 0 (q is negated), else 0
 };
 
 constexpr f32x16 kZero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
@@ -127,6 +138,7 @@ __global__ void __launch_bounds__(256, 2)
 prefill_kernel(PParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t ks_buf[2][kTile * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t vt_buf[2][kD * kVRow];
+  __shared__ u32x4 qs_buf[4][2 * 4 * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -154,31 +166,32 @@ prefill_kernel(PParams p) {
   const int h = 4 * g + wave;
   const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks;
 
-  // Q^T operand: lane holds q row (qt*32 + lane%32), d in [ks*16 + 8*(lane/32), +8)
+  // Q^T operand, kept in LDS: lane holds q row (qt*32 + lane%32), d in
+  // [k*16 + 8*(lane/32), +8)
   const int lr = lane & 31, lh = lane >> 5;
-  bf16x8_t qop[2][4];
+  u32x4* qsw = qs_buf[wave];  // this wavefront's Q^T operand [qt][k][lane]
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     int row = q0 + qt * 32 + lr;
     row = row < q_len ? row : q_len - 1;
     const uint16_t* qr = p.q + ((int64_t)(qs + row) * p.Hq + h) * kD + 8 * lh;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qr + 16 * k);
-      v ^= u32x4{p.q_sign, p.q_sign, p.q_sign, p.q_sign};
-      qop[qt][k] = as_bf16x8(v);
-    }
+    for (int k = 0; k < 4; ++k)
+      qsw[(qt * 4 + k) * 64 + lane] = *reinterpret_cast<const u32x4*>(qr + 16 * k) ^
+                                      u32x4{p.q_sign, p.q_sign, p.q_sign, p.q_sign};
   }
 
   f32x16 o[2][2];  // [dt][qt]
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[a][c][r] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
+    for (int c = 0; c < 2; ++c) o[a][c] = kZero16;
+  // Reference max m per query column (log2 units): weights are
+  // exp2(c * s - m).  has_ref is false until the column has seen a visible key.
+  float m_ref[2] = {0.f, 0.f};
+  bool has_ref[2] = {false, false};
+  const float c2 = p.c_log2;
+  float l_run[2] = {0.f, 0.f};  // this lane's share of the row sum
 
   // K/V tiles go global -> registers -> LDS one tile ahead of the MFMAs, and
   // the block id of the tile after that is read one more tile ahead, so no
@@ -199,7 +212,7 @@ prefill_kernel(PParams p) {
     const uint16_t* ks = ks_buf[buf];
     const uint16_t* vt = vt_buf[buf];
 
-    // S^T = K . Q^T  (scores before scaling); the first k-step starts from 0
+    // S^T = K . Q^T  (scores before scaling)
     f32x16 s[2][2];  // [kt][qt]
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -207,8 +220,10 @@ prefill_kernel(PParams p) {
       for (int k = 0; k < 4; ++k) {
         const bf16x8_t a = as_bf16x8(
             *reinterpret_cast<const u32x4*>(ks + (kt * 32 + lr) * kKRow + 16 * k + 8 * lh));
-        s[kt][0] = mfma(a, qop[0][k], k == 0 ? kZero16 : s[kt][0]);
-        s[kt][1] = mfma(a, qop[1][k], k == 0 ? kZero16 : s[kt][1]);
+        const bf16x8_t q0 = as_bf16x8(qsw[(0 * 4 + k) * 64 + lane]);
+        const bf16x8_t q1 = as_bf16x8(qsw[(1 * 4 + k) * 64 + lane]);
+        s[kt][0] = mfma(a, q0, k == 0 ? kZero16 : s[kt][0]);
+        s[kt][1] = mfma(a, q1, k == 0 ? kZero16 : s[kt][1]);
       }
     }
 
@@ -227,66 +242,69 @@ prefill_kernel(PParams p) {
       }
     }
 
-    // Online softmax per query column (lane%32 of each qt), log2 domain.  The
-    // running max m_run is moved only when a column's tile max exceeds it by
-    // more than kLazyLog2; otherwise weights are exp2(score - m_run) <= 2^8
-    // and the accumulator is left alone (same result by the softmax shift
-    // identity).  The decision is wave-uniform.
-    float mx[2];
-    bool move = false;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      float v = fmaxf(s[0][qt][0], s[0][qt][1]);
-#pragma unroll
-      for (int r = 2; r < 16; ++r) v = fmaxf(v, s[0][qt][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v = fmaxf(v, s[1][qt][r]);
-      mx[qt] = fmaxf(v, shfl_xor(v, 32)) * p.scale_log2;
-      move = move || mx[qt] > m_run[qt] + kLazyLog2;
-    }
-    if (__builtin_amdgcn_ballot_w64(move) != 0) {
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const float m_new = fmaxf(m_run[qt], mx[qt]);
-        // m_run = -inf: nothing accumulated yet, alpha = 0
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[qt] - m_new);
-        m_run[qt] = m_new;
-        l_run[qt] *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][qt][r] *= alpha;
-      }
-    }
-
-    // P^T operand [qt][key step] as bf16; the row sums add the same rounded
-    // weights that P.V uses (v_dot2 against (1, 1))
+    // Weights against the reference: P^T operand as bf16, and this lane's
+    // partial row sums of the same rounded weights (v_dot2 against (1, 1)).
     bf16x8_t pop[2][4];
+    float lsum[2];
+    auto weights = [&](int qt, float m) {
+      float l0 = 0.f, l1 = 0.f;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const float m_use = m_run[qt] == -INFINITY ? 0.f : m_run[qt];
-      float lsum0 = 0.f, lsum1 = 0.f;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           u32x4 w;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 8 * half + 2 * e;
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][r], p.scale_log2, -m_use));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][r + 1], p.scale_log2, -m_use));
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][r], c2, -m));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][r + 1], c2, -m));
             w[e] = pack_bf16(p0, p1);
             if (e & 1)
-              lsum1 = dot2_bf16(w[e], kOnesBf16x2, lsum1);
+              l1 = dot2_bf16(w[e], kOnesBf16x2, l1);
             else
-              lsum0 = dot2_bf16(w[e], kOnesBf16x2, lsum0);
+              l0 = dot2_bf16(w[e], kOnesBf16x2, l0);
           }
           pop[qt][2 * kt + half] = as_bf16x8(w);
         }
+      lsum[qt] = l0 + l1;
+    };
+    weights(0, m_ref[0]);
+    weights(1, m_ref[1]);
+
+    // Exact-max path, wave-uniform and rare: a weight may exceed the bound
+    // (a score rose well above the reference), or a column has no reference
+    // yet.  The reference moves up to the tile max, the accumulator and row
+    // sum are rescaled, and the weights are formed again.  By the softmax
+    // shift identity the result does not depend on the reference used.
+    bool redo = false;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) redo = redo || !(lsum[qt] <= kLazyBound) || !has_ref[qt];
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float v = fmaxf(s[0][qt][0], s[0][qt][1]);
+#pragma unroll
+        for (int r = 2; r < 16; ++r) v = fmaxf(v, s[0][qt][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v = fmaxf(v, s[1][qt][r]);
+        const float mx = fmaxf(v, shfl_xor(v, 32)) * c2;  // tile max, log2 units
+        // no visible key yet: stay without a reference (weights are 0)
+        if (mx != -INFINITY && mx == mx) {
+          const float m_new = has_ref[qt] ? fmaxf(m_ref[qt], mx) : mx;
+          const float alpha = has_ref[qt] ? __builtin_amdgcn_exp2f(m_ref[qt] - m_new) : 0.f;
+          l_run[qt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[dt][qt][r] *= alpha;
+          m_ref[qt] = m_new;
+          has_ref[qt] = true;
+        }
+        weights(qt, m_ref[qt]);
       }
-      l_run[qt] += lsum0 + lsum1;
     }
+    l_run[0] += lsum[0];
+    l_run[1] += lsum[1];
 
     // O^T += V^T . P^T
 #pragma unroll
@@ -353,8 +371,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.tiles_max = (a.max_q_len + kTile - 1) / kTile;
   // |scale| in log2 units, floored so that a zero scale still maps masked
   // (-inf) scores to -inf instead of NaN; any real score times 1e-30 is 0.
-  p.scale_log2 = (a.scale < 0.f ? -a.scale : a.scale) * kLog2e;
-  if (p.scale_log2 < 1e-30f) p.scale_log2 = 1e-30f;
+  p.c_log2 = (a.scale < 0.f ? -a.scale : a.scale) * kLog2e;
+  if (p.c_log2 < 1e-30f) p.c_log2 = 1e-30f;
   p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
   const int64_t grid = (int64_t)p.tiles_max * a.B * a.Hkv;
   hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
