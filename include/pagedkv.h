@@ -124,7 +124,8 @@ PKV_API size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int3
  * partition_size  PKV_PARTITION_NONE: each (sequence, KV head) in one
  *               wavefront.  A positive multiple of block_size: each sequence
  *               is split at multiples of that many tokens, partitions run in
- *               parallel and a second kernel merges them by log-sum-exp.
+ *               parallel and the wavefront that finishes a sequence's last
+ *               partition merges them by log-sum-exp (no second kernel).
  *               PKV_PARTITION_AUTO: all blocks of the batch are cut into equal
  *               shares, one per wavefront of a fixed grid, and streams cut
  *               across shares are merged the same way.
@@ -135,7 +136,10 @@ PKV_API size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int3
  *               call leaves at zero again, so one zero-fill serves all later
  *               calls, whatever their shapes.  Calls that share a workspace
  *               must not run concurrently (they would race on it).  Splits
- *               handle up to 32768 (sequence, KV head) streams.
+ *               handle up to 32768 (sequence, KV head) streams and up to
+ *               2^21 - 1 partial records (B * Hkv * partitions per sequence
+ *               for a fixed partition_size, 4096 for PKV_PARTITION_AUTO);
+ *               beyond either limit the call returns PKV_ERR_UNSUPPORTED.
  * This build implements D == 64, block_size == 16 and Hq == 4 * Hkv
  * (PKV_ERR_UNSUPPORTED otherwise).  Empty contexts give zero rows.
  */

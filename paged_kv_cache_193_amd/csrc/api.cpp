@@ -79,6 +79,12 @@ int plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_siz
     if ((int64_t)B * Hkv > pkv::kMaxSplitStreams)
       return fail(PKV_ERR_UNSUPPORTED, "split decode handles B*Hkv <= %d streams (got %lld)",
                   pkv::kMaxSplitStreams, (long long)B * Hkv);
+    // the kernels address the records with 32-bit byte offsets
+    if (plan->records > (size_t)pkv::kMaxRecords)
+      return fail(PKV_ERR_UNSUPPORTED,
+                  "split decode needs %zu partial records, at most %d are supported: use a "
+                  "larger partition_size",
+                  plan->records, pkv::kMaxRecords);
     // counter region, then records (normalised outputs) and their (m, l) pairs
     plan->bytes = pkv::kCounterBytes + plan->records * (pkv::kRecordFloats + 8) * sizeof(float);
   }

@@ -51,9 +51,12 @@ constexpr int kD = 64;
 constexpr int kBS = 16;
 constexpr int kWaves = 4;        // wavefronts per workgroup
 #ifndef PKV_DECODE_RING
-#define PKV_DECODE_RING 4
+#define PKV_DECODE_RING 2
 #endif
 constexpr int kRing = PKV_DECODE_RING;  // K/V blocks in flight per wavefront
+#ifndef PKV_MERGE_BATCH
+#define PKV_MERGE_BATCH 16
+#endif
 
 struct BlockRegs {
   u32x4 ka, kb, va, vb;  // tokens grp and grp+8, head_dim chunk i
@@ -79,7 +82,24 @@ struct Params {
   float* ws_o;
   float* ws_ml;
   uint32_t* ws_count;  // per stream (b, g): split records written so far
+  int n_records;       // records in ws_o / ws_ml
 };
+
+// Split records are written and read with 16-byte buffer accesses at agent
+// scope (sc1), so a piece written by one XCD is seen by a wave merging on
+// another.  The buffer descriptors also bound every access to the records.
+constexpr int kSc1 = 16;                    // cache-policy bit of buffer ops
+constexpr int kRsrcWord3 = 0x00020000;      // raw buffer, dword data
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t records_o(const Params& p) {
+  return __builtin_amdgcn_make_buffer_rsrc(p.ws_o, (short)0, p.n_records * kRecordFloats * 4,
+                                           kRsrcWord3);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t records_ml(const Params& p) {
+  return __builtin_amdgcn_make_buffer_rsrc(p.ws_ml, (short)0, p.n_records * 8 * 4, kRsrcWord3);
+}
 
 // Where the split records of one stream live: piece k of the stream is
 // record base + k * stride (+ first_extra for k == 0).
@@ -348,17 +368,14 @@ __device__ __forceinline__ void finish_segment(const LaneState& st, const Params
     }
     return;
   }
-  // Split stream: write this piece's record with agent-scope (sc1) stores;
-  // publish_piece() counts it once the stores have completed.
-  float* ro = p.ws_o + (int64_t)record * kRecordFloats + h * kD + d4;
-  __hip_atomic_store(ro + 0, o.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(ro + 1, o.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(ro + 2, o.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(ro + 3, o.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // Split stream: write this piece's record (agent-scope stores, one 1 KB
+  // row of o per wave); count_piece() counts it once the stores completed.
+  const f32x4 ov = {o.x, o.y, o.z, o.w};
+  __builtin_amdgcn_raw_buffer_store_b128(ov, records_o(p), (record * kRecordFloats + h * kD + d4) * 4,
+                                         0, kSc1);
   if ((lane & 15) == 0) {
-    float* rml = p.ws_ml + ((int64_t)record * 4 + h) * 2;
-    __hip_atomic_store(rml + 0, m_h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(rml + 1, l_h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const f32x2 ml = {m_h, l_h};
+    __builtin_amdgcn_raw_buffer_store_b64(ml, records_ml(p), (record * 4 + h) * 8, 0, kSc1);
   }
 }
 
@@ -375,51 +392,108 @@ __device__ __forceinline__ void drain_stores() {
 // all pieces by log-sum-exp and re-zeroes the counter.  Records are read with
 // agent-scope (sc1) loads and the counter is an agent-scope atomic, so pieces
 // written on other XCDs are seen without any cache flush.
-__device__ __forceinline__ void publish_piece(const Params& p, int b, int g,
-                                              const RecordList& rl, int lane) {
+// The wave whose count_piece() brings a stream's count to its number of pieces
+// merges all of them by log-sum-exp,
+//   out_h = sum_k w_k,h o_k,h / sum_k w_k,h,   w_k,h = l_k,h 2^(m_k,h - M_h),
+// writes the rows and resets the counter.  The pieces' (m, l) are staged in
+// this wave's LDS area `red` (64 pieces at a time, one piece per lane) and
+// every lane forms its head's maximum and weights itself, so the merge needs
+// no cross-lane reductions; the o rows are read kBatch pieces per round trip,
+// the first batch together with the (m, l) of the first chunk.
+// Add one finished piece to stream (b, g)'s count (agent-scope atomic, issued
+// by lane 0); returns the count before the addition, in every lane.
+__device__ __forceinline__ uint32_t count_piece(const Params& p, int b, int g, int lane) {
+  uint32_t before = 0;
+  if (lane == 0)
+    before = __hip_atomic_fetch_add(p.ws_count + (int64_t)b * p.Hkv + g, 1u, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_amdgcn_readfirstlane(before);
+}
+
+__device__ __forceinline__ void merge_stream(const Params& p, int b, int g, const RecordList& rl,
+                                             float* red, int lane) {
   const int h = lane >> 4;
   const int d4 = (lane & 15) * 4;
   uint32_t* cnt = p.ws_count + (int64_t)b * p.Hkv + g;
-  uint32_t before = 0;
-  if (lane == 0) before = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  before = __builtin_amdgcn_readfirstlane(before);
-  if (before + 1 != (uint32_t)rl.pieces) return;
+  const int P = rl.pieces;
 
-  // last piece in: merge all pieces of the stream, 8 pieces per round so their
-  // loads are in flight together
-  constexpr int kBatch = 8;
-  float M = -INFINITY, den = 0.f;
-  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k0 = 0; k0 < rl.pieces; k0 += kBatch) {
-    float bm[kBatch], bl[kBatch];
-    float4 bo[kBatch];
+  const __amdgpu_buffer_rsrc_t rso = records_o(p);
+  const __amdgpu_buffer_rsrc_t rsml = records_ml(p);
+  auto rec = [&](int k) -> int {
+    return (int)(rl.base + (int64_t)k * rl.stride + (k == 0 ? rl.first_extra : 0));
+  };
+  constexpr int kBatch = PKV_MERGE_BATCH;  // o rows per round trip
+  const int o_off = (h * kD + d4) * 4;
+
+  // o rows of the first batch (clamped repeats get weight 0)
+  f32x4 ob[kBatch];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int k = k0 + u < rl.pieces ? k0 + u : rl.pieces - 1;  // repeats are skipped below
-      const int64_t r = rl.base + (int64_t)k * rl.stride + (k == 0 ? rl.first_extra : 0);
-      const float* pml = p.ws_ml + (r * 4 + h) * 2;
-      const float* po = p.ws_o + r * kRecordFloats + h * kD + d4;
-      bm[u] = __hip_atomic_load(pml + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      bl[u] = __hip_atomic_load(pml + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      bo[u].x = __hip_atomic_load(po + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      bo[u].y = __hip_atomic_load(po + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      bo[u].z = __hip_atomic_load(po + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      bo[u].w = __hip_atomic_load(po + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+  for (int u = 0; u < kBatch; ++u)
+    ob[u] = __builtin_amdgcn_raw_buffer_load_b128(
+        rso, rec(u < P ? u : P - 1) * (kRecordFloats * 4) + o_off, 0, kSc1);
+
+  // (m, l) of pieces c0 .. c0+63, head-major: red[head * 128 + 2 * k + {0, 1}];
+  // pieces past the end get l = 0 (no weight)
+  auto stage = [&](int c0) {
+    const int k = c0 + lane;
+    const int r = rec(k < P ? k : P - 1);
+    f32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rsml, r * 32, 0, kSc1);
+    f32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rsml, r * 32 + 16, 0, kSc1);
+    if (k >= P) lo[1] = lo[3] = hi[1] = hi[3] = 0.f;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();  // earlier readers of red are done
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    *reinterpret_cast<f32x2*>(red + 0 * 128 + 2 * lane) = f32x2{lo[0], lo[1]};
+    *reinterpret_cast<f32x2*>(red + 1 * 128 + 2 * lane) = f32x2{lo[2], lo[3]};
+    *reinterpret_cast<f32x2*>(red + 2 * 128 + 2 * lane) = f32x2{hi[0], hi[1]};
+    *reinterpret_cast<f32x2*>(red + 3 * 128 + 2 * lane) = f32x2{hi[2], hi[3]};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  const float* rh = red + h * 128;
+
+  // pass 1: this lane's head maximum over all pieces
+  float M = -INFINITY;
+  for (int c0 = 0; c0 < P; c0 += 64) {
+    stage(c0);
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      if (k0 + u >= rl.pieces || !(bl[u] > 0.f)) continue;
-      const float Mn = fmaxf(M, bm[u]);
-      const float a = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-      const float wk = bl[u] * __builtin_amdgcn_exp2f(bm[u] - Mn);
-      num = make_float4(num.x * a + wk * bo[u].x, num.y * a + wk * bo[u].y,
-                        num.z * a + wk * bo[u].z, num.w * a + wk * bo[u].w);
-      den = den * a + wk;
-      M = Mn;
+    for (int k = 0; k < 64; k += 2) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(rh + 2 * k);  // (m, l) of k, k+1
+      M = fmaxf(M, v[1] > 0.f ? v[0] : -INFINITY);
+      M = fmaxf(M, v[3] > 0.f ? v[2] : -INFINITY);
     }
   }
-  const float inv2 = den > 0.f ? 1.0f / den : 0.f;
-  const float4 res = make_float4(num.x * inv2, num.y * inv2, num.z * inv2, num.w * inv2);
+
+  // pass 2: weights and the weighted sum of the o rows
+  float den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < P; c0 += 64) {
+    if (P > 64) stage(c0);  // else chunk 0 is still staged
+    const int n = P - c0 < 64 ? P - c0 : 64;
+    for (int k0 = 0; k0 < n; k0 += kBatch) {
+      if (c0 + k0 > 0) {
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int k = c0 + k0 + u;
+          ob[u] = __builtin_amdgcn_raw_buffer_load_b128(
+              rso, rec(k < P ? k : P - 1) * (kRecordFloats * 4) + o_off, 0, kSc1);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; u += 2) {
+        // pieces k0+u, k0+u+1 (a staged slot past n has l = 0 or is masked here)
+        const int kk = k0 + u < 64 - 1 ? k0 + u : 62;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(rh + 2 * kk);
+        const float w0 = (k0 + u < n && v[1] > 0.f) ? v[1] * __builtin_amdgcn_exp2f(v[0] - M) : 0.f;
+        const float w1 = (k0 + u + 1 < n && v[3] > 0.f) ? v[3] * __builtin_amdgcn_exp2f(v[2] - M) : 0.f;
+        den += w0 + w1;
+        num += w0 * ob[u] + w1 * ob[u + 1];
+      }
+    }
+  }
+  const float inv = den > 0.f ? 1.0f / den : 0.f;
+  const float4 res = make_float4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
   const int64_t row = ((int64_t)b * p.Hq + 4 * g + h) * kD + d4;
   if (p.out_f32) {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row) = res;
@@ -476,7 +550,7 @@ decode_units_kernel(Params p) {
   finish_segment(st, p, b, g, complete, unit, rl, red[wave], lane);
   if (!complete) {
     drain_stores();
-    publish_piece(p, b, g, rl, lane);
+    if (count_piece(p, b, g, lane) + 1 == (uint32_t)rl.pieces) merge_stream(p, b, g, rl, red[wave], lane);
   }
 }
 
@@ -799,8 +873,11 @@ decode_auto_kernel(Params p) {
   // segment in the middle of the stream
   if (pend) {
     drain_stores();
-    publish_piece(p, pb0, pg0, prl0, lane);
-    if (pend > 1) publish_piece(p, pb1, pg1, prl1, lane);
+    // both counts go out before either result is needed
+    const uint32_t c0 = count_piece(p, pb0, pg0, lane);
+    const uint32_t c1 = pend > 1 ? count_piece(p, pb1, pg1, lane) : 0u;
+    if (c0 + 1 == (uint32_t)prl0.pieces) merge_stream(p, pb0, pg0, prl0, red[wave], lane);
+    if (pend > 1 && c1 + 1 == (uint32_t)prl1.pieces) merge_stream(p, pb1, pg1, prl1, red[wave], lane);
   }
 }
 
@@ -834,6 +911,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.ws_o = a.ws_o;
   p.ws_ml = a.ws_ml;
   p.ws_count = a.ws_count;
+  p.n_records = (int)decode_records(a.mode, a.B, a.Hkv, a.parts_max);
   const int streams = a.B * a.Hkv;
   if (a.mode == kWhole) {
     const int grid = (streams + kWaves - 1) / kWaves;

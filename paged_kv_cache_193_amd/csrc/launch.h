@@ -39,6 +39,8 @@ constexpr int kRecordFloats = 4 * 64;
 // region at the start of the workspace, whatever the call's shapes, so a
 // workspace zero-filled once stays valid for every later call.
 constexpr int kMaxSplitStreams = 32768;
+// Split records addressable with 32-bit byte offsets (1 KB of output each).
+constexpr int kMaxRecords = (1 << 21) - 1;
 constexpr size_t kCounterBytes = (size_t)kMaxSplitStreams * 4;
 
 struct DecodeArgs {

@@ -79,6 +79,8 @@ def decode_call(lib, **kw):
     (dict(part=512, maxctx=4096), pkv.PKV_ERR_WORKSPACE),
     (dict(part=-1), pkv.PKV_ERR_WORKSPACE),
     (dict(part=-1, B=5000), pkv.PKV_ERR_UNSUPPORTED),
+    # 32768 streams x 64 partitions: more split records than 32-bit offsets reach
+    (dict(part=16, B=4096, maxb=64, maxctx=1024), pkv.PKV_ERR_UNSUPPORTED),
 ])
 def test_decode_rejects(lib, kw, code):
     assert decode_call(lib, **kw) == code
