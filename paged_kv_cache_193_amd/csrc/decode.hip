@@ -55,7 +55,7 @@ constexpr int kWaves = 4;        // wavefronts per workgroup
 #endif
 constexpr int kRing = PKV_DECODE_RING;  // K/V blocks in flight per wavefront
 #ifndef PKV_MERGE_BATCH
-#define PKV_MERGE_BATCH 16
+#define PKV_MERGE_BATCH 32
 #endif
 
 struct BlockRegs {
@@ -392,14 +392,6 @@ __device__ __forceinline__ void drain_stores() {
 // all pieces by log-sum-exp and re-zeroes the counter.  Records are read with
 // agent-scope (sc1) loads and the counter is an agent-scope atomic, so pieces
 // written on other XCDs are seen without any cache flush.
-// The wave whose count_piece() brings a stream's count to its number of pieces
-// merges all of them by log-sum-exp,
-//   out_h = sum_k w_k,h o_k,h / sum_k w_k,h,   w_k,h = l_k,h 2^(m_k,h - M_h),
-// writes the rows and resets the counter.  The pieces' (m, l) are staged in
-// this wave's LDS area `red` (64 pieces at a time, one piece per lane) and
-// every lane forms its head's maximum and weights itself, so the merge needs
-// no cross-lane reductions; the o rows are read kBatch pieces per round trip,
-// the first batch together with the (m, l) of the first chunk.
 // Add one finished piece to stream (b, g)'s count (agent-scope atomic, issued
 // by lane 0); returns the count before the addition, in every lane.
 __device__ __forceinline__ uint32_t count_piece(const Params& p, int b, int g, int lane) {
@@ -410,98 +402,158 @@ __device__ __forceinline__ uint32_t count_piece(const Params& p, int b, int g, i
   return __builtin_amdgcn_readfirstlane(before);
 }
 
-__device__ __forceinline__ void merge_stream(const Params& p, int b, int g, const RecordList& rl,
-                                             float* red, int lane) {
+// A stream whose pieces this wave merges.
+struct MergeJob {
+  int b, g;
+  RecordList rl;
+};
+
+// Largest value / sum over the 64 lanes, returned wave-uniform: rotations
+// inside each row of 16 (DPP), then the four row results by readlane.
+__device__ __forceinline__ float wave_max_u(float v) {
+  v = fmaxf(v, dpp<kRowRor8>(v));
+  v = fmaxf(v, dpp<kRowRor4>(v));
+  v = fmaxf(v, dpp<kRowRor2>(v));
+  v = fmaxf(v, dpp<kRowRor1>(v));
+  const int iv = __builtin_bit_cast(int, v);
+  return fmaxf(fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16))),
+               fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)),
+                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48))));
+}
+__device__ __forceinline__ float wave_sum_u(float v) {
+  v += dpp<kRowRor8>(v);
+  v += dpp<kRowRor4>(v);
+  v += dpp<kRowRor2>(v);
+  v += dpp<kRowRor1>(v);
+  const int iv = __builtin_bit_cast(int, v);
+  return (__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 0)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 16))) +
+         (__builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 32)) +
+          __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48)));
+}
+
+// Merge the pieces of N (1 or 2) streams by log-sum-exp,
+//   out_h = sum_k w_k,h o_k,h / sum_k w_k,h,   w_k,h = l_k,h 2^(m_k,h - M_h),
+// write their rows and reset their counters.  Every read goes out before any
+// result is needed: the (m, l) of up to 64 pieces per stream (piece k in lane
+// k) and the o rows of the first kB pieces per stream, so merging two streams
+// of few pieces costs one round trip.  M_h and the sums are wave reductions;
+// the weights reach the lanes that accumulate head h through this wave's LDS
+// area `red` (head-major, 4 pieces per read).
+template <int N>
+__device__ __forceinline__ void merge_streams(const Params& p, const MergeJob (&job)[N],
+                                              float* red, int lane) {
   const int h = lane >> 4;
   const int d4 = (lane & 15) * 4;
-  uint32_t* cnt = p.ws_count + (int64_t)b * p.Hkv + g;
-  const int P = rl.pieces;
-
   const __amdgpu_buffer_rsrc_t rso = records_o(p);
   const __amdgpu_buffer_rsrc_t rsml = records_ml(p);
-  auto rec = [&](int k) -> int {
+  constexpr int kB = PKV_MERGE_BATCH / N;  // o rows per stream per round trip
+  static_assert(kB % 4 == 0, "o rows are weighted 4 pieces per LDS read");
+  const int o_off = (h * kD + d4) * 4;
+  auto rec = [&](int n, int k) -> int {
+    const RecordList& rl = job[n].rl;
     return (int)(rl.base + (int64_t)k * rl.stride + (k == 0 ? rl.first_extra : 0));
   };
-  constexpr int kBatch = PKV_MERGE_BATCH;  // o rows per round trip
-  const int o_off = (h * kD + d4) * 4;
-
-  // o rows of the first batch (clamped repeats get weight 0)
-  f32x4 ob[kBatch];
-#pragma unroll
-  for (int u = 0; u < kBatch; ++u)
-    ob[u] = __builtin_amdgcn_raw_buffer_load_b128(
-        rso, rec(u < P ? u : P - 1) * (kRecordFloats * 4) + o_off, 0, kSc1);
-
-  // (m, l) of pieces c0 .. c0+63, head-major: red[head * 128 + 2 * k + {0, 1}];
-  // pieces past the end get l = 0 (no weight)
-  auto stage = [&](int c0) {
+  auto load_o = [&](int n, int k) -> f32x4 {
+    const int P = job[n].rl.pieces;
+    return __builtin_amdgcn_raw_buffer_load_b128(
+        rso, rec(n, k < P ? k : P - 1) * (kRecordFloats * 4) + o_off, 0, kSc1);
+  };
+  // (m, l) of piece c0 + lane of stream n: (m0 l0 m1 l1), (m2 l2 m3 l3)
+  auto load_ml = [&](int n, int c0, f32x4& lo, f32x4& hi) {
+    const int P = job[n].rl.pieces;
     const int k = c0 + lane;
-    const int r = rec(k < P ? k : P - 1);
-    f32x4 lo = __builtin_amdgcn_raw_buffer_load_b128(rsml, r * 32, 0, kSc1);
-    f32x4 hi = __builtin_amdgcn_raw_buffer_load_b128(rsml, r * 32 + 16, 0, kSc1);
-    if (k >= P) lo[1] = lo[3] = hi[1] = hi[3] = 0.f;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();  // earlier readers of red are done
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    *reinterpret_cast<f32x2*>(red + 0 * 128 + 2 * lane) = f32x2{lo[0], lo[1]};
-    *reinterpret_cast<f32x2*>(red + 1 * 128 + 2 * lane) = f32x2{lo[2], lo[3]};
-    *reinterpret_cast<f32x2*>(red + 2 * 128 + 2 * lane) = f32x2{hi[0], hi[1]};
-    *reinterpret_cast<f32x2*>(red + 3 * 128 + 2 * lane) = f32x2{hi[2], hi[3]};
+    const int r = rec(n, k < P ? k : P - 1);
+    lo = __builtin_amdgcn_raw_buffer_load_b128(rsml, r * 32, 0, kSc1);
+    hi = __builtin_amdgcn_raw_buffer_load_b128(rsml, r * 32 + 16, 0, kSc1);
+  };
+  // this lane's piece: m and l per head, l = 0 past the stream's pieces
+  auto unpack = [&](int n, int c0, const f32x4& lo, const f32x4& hi, float (&m)[4],
+                    float (&l)[4]) {
+    const bool in = c0 + lane < job[n].rl.pieces;
+    m[0] = lo[0]; m[1] = lo[2]; m[2] = hi[0]; m[3] = hi[2];
+    l[0] = in ? lo[1] : 0.f; l[1] = in ? lo[3] : 0.f;
+    l[2] = in ? hi[1] : 0.f; l[3] = in ? hi[3] : 0.f;
+  };
+  auto lds_sync = [&]() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
-  const float* rh = red + h * 128;
 
-  // pass 1: this lane's head maximum over all pieces
-  float M = -INFINITY;
-  for (int c0 = 0; c0 < P; c0 += 64) {
-    stage(c0);
+  f32x4 ob[N][kB];
+  f32x4 ml_lo[N], ml_hi[N];
 #pragma unroll
-    for (int k = 0; k < 64; k += 2) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(rh + 2 * k);  // (m, l) of k, k+1
-      M = fmaxf(M, v[1] > 0.f ? v[0] : -INFINITY);
-      M = fmaxf(M, v[3] > 0.f ? v[2] : -INFINITY);
-    }
+  for (int n = 0; n < N; ++n) {
+    load_ml(n, 0, ml_lo[n], ml_hi[n]);
+#pragma unroll
+    for (int u = 0; u < kB; ++u) ob[n][u] = load_o(n, u);
   }
 
-  // pass 2: weights and the weighted sum of the o rows
-  float den = 0.f;
-  f32x4 num = {0.f, 0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < P; c0 += 64) {
-    if (P > 64) stage(c0);  // else chunk 0 is still staged
-    const int n = P - c0 < 64 ? P - c0 : 64;
-    for (int k0 = 0; k0 < n; k0 += kBatch) {
-      if (c0 + k0 > 0) {
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int k = c0 + k0 + u;
-          ob[u] = __builtin_amdgcn_raw_buffer_load_b128(
-              rso, rec(k < P ? k : P - 1) * (kRecordFloats * 4) + o_off, 0, kSc1);
+  for (int n = 0; n < N; ++n) {
+    const int P = job[n].rl.pieces;
+    float m[4], l[4], M[4];
+    unpack(n, 0, ml_lo[n], ml_hi[n], m, l);
+    // maxima over all pieces (l > 0 only)
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) M[hh] = wave_max_u(l[hh] > 0.f ? m[hh] : -INFINITY);
+    for (int c0 = 64; c0 < P; c0 += 64) {
+      f32x4 lo, hi;
+      float mc[4], lc[4];
+      load_ml(n, c0, lo, hi);
+      unpack(n, c0, lo, hi, mc, lc);
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh)
+        M[hh] = fmaxf(M[hh], wave_max_u(lc[hh] > 0.f ? mc[hh] : -INFINITY));
+    }
+    float* wr = red + n * 256;  // weights [head][64 pieces]
+    float den_h = 0.f;
+    f32x4 num = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < P; c0 += 64) {
+      if (c0 > 0) {
+        f32x4 lo, hi;
+        load_ml(n, c0, lo, hi);
+        unpack(n, c0, lo, hi, m, l);
+      }
+      lds_sync();  // earlier readers of wr are done
+#pragma unroll
+      for (int hh = 0; hh < 4; ++hh) {
+        const float w = l[hh] > 0.f ? l[hh] * __builtin_amdgcn_exp2f(m[hh] - M[hh]) : 0.f;
+        wr[hh * 64 + lane] = w;
+        const float t = wave_sum_u(w);
+        den_h = hh == h ? den_h + t : den_h;
+      }
+      lds_sync();
+      const int cn = P - c0 < 64 ? P - c0 : 64;
+      for (int k0 = 0; k0 < cn; k0 += kB) {
+        if (c0 + k0 > 0) {
+#pragma unroll
+          for (int u = 0; u < kB; ++u) ob[n][u] = load_o(n, c0 + k0 + u);
+        }
+#pragma unroll
+        for (int u = 0; u < kB; u += 4) {
+          // weights of pieces k0+u .. k0+u+3 (0 past the stream's pieces)
+          const f32x4 w4 = *reinterpret_cast<const f32x4*>(wr + h * 64 + (k0 + u < 60 ? k0 + u : 60));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) num += w4[e] * ob[n][u + e];
         }
       }
-#pragma unroll
-      for (int u = 0; u < kBatch; u += 2) {
-        // pieces k0+u, k0+u+1 (a staged slot past n has l = 0 or is masked here)
-        const int kk = k0 + u < 64 - 1 ? k0 + u : 62;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(rh + 2 * kk);
-        const float w0 = (k0 + u < n && v[1] > 0.f) ? v[1] * __builtin_amdgcn_exp2f(v[0] - M) : 0.f;
-        const float w1 = (k0 + u + 1 < n && v[3] > 0.f) ? v[3] * __builtin_amdgcn_exp2f(v[2] - M) : 0.f;
-        den += w0 + w1;
-        num += w0 * ob[u] + w1 * ob[u + 1];
-      }
     }
+    const float inv = den_h > 0.f ? 1.0f / den_h : 0.f;
+    const float4 res = make_float4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
+    const int64_t row = ((int64_t)job[n].b * p.Hq + 4 * job[n].g + h) * kD + d4;
+    if (p.out_f32) {
+      *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row) = res;
+    } else {
+      u32x2 pk = {pack_bf16(res.x, res.y), pack_bf16(res.z, res.w)};
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + row) = pk;
+    }
+    if (lane == 0)
+      __hip_atomic_store(p.ws_count + (int64_t)job[n].b * p.Hkv + job[n].g, 0u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
-  const float inv = den > 0.f ? 1.0f / den : 0.f;
-  const float4 res = make_float4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
-  const int64_t row = ((int64_t)b * p.Hq + 4 * g + h) * kD + d4;
-  if (p.out_f32) {
-    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row) = res;
-  } else {
-    u32x2 pk = {pack_bf16(res.x, res.y), pack_bf16(res.z, res.w)};
-    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + row) = pk;
-  }
-  if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void write_zero_rows(const Params& p, int b, int g, int lane) {
@@ -550,7 +602,10 @@ decode_units_kernel(Params p) {
   finish_segment(st, p, b, g, complete, unit, rl, red[wave], lane);
   if (!complete) {
     drain_stores();
-    if (count_piece(p, b, g, lane) + 1 == (uint32_t)rl.pieces) merge_stream(p, b, g, rl, red[wave], lane);
+    if (count_piece(p, b, g, lane) + 1 == (uint32_t)rl.pieces) {
+      const MergeJob job[1] = {{b, g, rl}};
+      merge_streams<1>(p, job, red[wave], lane);
+    }
   }
 }
 
@@ -876,8 +931,15 @@ decode_auto_kernel(Params p) {
     // both counts go out before either result is needed
     const uint32_t c0 = count_piece(p, pb0, pg0, lane);
     const uint32_t c1 = pend > 1 ? count_piece(p, pb1, pg1, lane) : 0u;
-    if (c0 + 1 == (uint32_t)prl0.pieces) merge_stream(p, pb0, pg0, prl0, red[wave], lane);
-    if (pend > 1 && c1 + 1 == (uint32_t)prl1.pieces) merge_stream(p, pb1, pg1, prl1, red[wave], lane);
+    const bool m0 = c0 + 1 == (uint32_t)prl0.pieces;
+    const bool m1 = pend > 1 && c1 + 1 == (uint32_t)prl1.pieces;
+    if (m0 && m1) {  // both streams: their reads share one round trip
+      const MergeJob job[2] = {{pb0, pg0, prl0}, {pb1, pg1, prl1}};
+      merge_streams<2>(p, job, red[wave], lane);
+    } else if (m0 || m1) {
+      const MergeJob job[1] = {m0 ? MergeJob{pb0, pg0, prl0} : MergeJob{pb1, pg1, prl1}};
+      merge_streams<1>(p, job, red[wave], lane);
+    }
   }
 }
 

@@ -39,6 +39,9 @@ enum : int {
   kQuadXor3 = 0x1B,        // quad_perm [3,2,1,0]
   kRowHalfMirror = 0x141,  // lane i <-> 7-i inside each group of 8
   kRowRor8 = 0x128,        // lane i <- lane (i+8) mod 16 inside each row of 16
+  kRowRor4 = 0x124,        // rotations of a row of 16 by 4, 2, 1 lanes
+  kRowRor2 = 0x122,
+  kRowRor1 = 0x121,
 };
 
 template <int kCtrl>
