@@ -3,19 +3,23 @@
 One step = one decode step of the ragged continuous-batching workload:
 64 sequences (context log-uniform in [16, 8192], block_size 16, 65536-block
 bf16 pool per layer, Llama-3.2-1B attention shapes: 32 query heads, 8 KV
-heads, head_dim 64), and for each of the 16 layers
-    kv_append (one new token per sequence)  ->  paged_attention_decode
-with the automatic balanced split (its log-sum-exp merge runs inside the
-decode kernel).  The step is captured once in a HIP graph and replayed.
+heads, head_dim 64), and for each of the 16 layers one
+    paged_attention_decode_append
+call: store one new token per sequence (kv_append) and attend to the whole
+context (paged_attention_decode) with the automatic balanced split, in one
+kernel launch whose log-sum-exp merge runs inside the kernel.  `--two-calls`
+times kv_append followed by paged_attention_decode per layer instead.  The
+step is captured once in a HIP graph and replayed.
 
 Prints ONE JSON line.  `value` is the whole step's algorithmic HBM bytes
 divided by the step time (inputs resident in HBM).  `roofline` is for the
-decode kernel alone (16 decode calls replayed as one HIP graph, timed with
-HIP events on the stream the graph runs on).  `cpu_baseline` is the CPU oracle on a bounded sample of the
-same workload.  `prefill` reports the causal paged prefill workload
-(4 x 512 + 2 x 2048 prompts) on the bf16 MFMA roofline.
+dominant kernel -- the combined append + decode kernel (the decode kernel
+with --two-calls) -- timed with HIP events over graph replays of its 16
+calls on the stream the graph runs on.  `cpu_baseline` is the CPU oracle on
+a bounded sample of the same workload.  `prefill` reports the causal paged
+prefill workload (4 x 512 + 2 x 2048 prompts) on the bf16 MFMA roofline.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--two-calls]
 """
 import argparse
 import hashlib
@@ -41,6 +45,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for counter scaling)")
+    ap.add_argument("--two-calls", action="store_true",
+                    help="kv_append then paged_attention_decode per layer (two launches)")
     ap.add_argument("--partition", type=int, default=-1,
                     help="decode partition_size (-1 = automatic balanced split)")
     return ap.parse_args()
@@ -66,9 +72,10 @@ def append_bytes(T_new, Hkv, D):
     return T_new * Hkv * D * 2 * 2 * 2  # K and V rows, read + write
 
 
-def traffic_from_profiles(kernel_hash):
-    """HBM bytes per decode call from committed counter runs, if they were
-    taken on this exact kernel source; else None."""
+def traffic_from_profiles(kernel_hash, fused):
+    """HBM bytes per launch of the timed kernel (combined append + decode, or
+    decode alone) from committed counter runs, if they were taken on this
+    exact kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "decode_ragged_traffic.json")
     try:
         with open(path) as f:
@@ -77,7 +84,7 @@ def traffic_from_profiles(kernel_hash):
         return None
     if rec.get("kernel_source_hash") != kernel_hash:
         return None
-    return rec.get("bytes_per_decode_call")
+    return rec.get("bytes_per_append_decode_call" if fused else "bytes_per_decode_call")
 
 
 def cpu_baseline(case, k_layers, v_layers, min_seconds=10.0):
@@ -116,9 +123,13 @@ def run_prefill(torch, pkv, wl, steps, warmup):
     for _ in range(warmup):
         pkv.paged_attention_prefill_causal(out, q, k, v, t, l, cu, p.scale, maxq)
     torch.cuda.synchronize()
+    # several calls per graph, so the gap between graph replays is not
+    # counted as kernel time
+    per_graph = 8
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        pkv.paged_attention_prefill_causal(out, q, k, v, t, l, cu, p.scale, maxq)
+        for _ in range(per_graph):
+            pkv.paged_attention_prefill_causal(out, q, k, v, t, l, cu, p.scale, maxq)
     graph.replay()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -127,7 +138,7 @@ def run_prefill(torch, pkv, wl, steps, warmup):
         graph.replay()
     ev1.record()
     torch.cuda.synchronize()
-    us = ev0.elapsed_time(ev1) / steps * 1e3
+    us = ev0.elapsed_time(ev1) / (steps * per_graph) * 1e3
     # visible (query, key) pairs: QK^T and PV, 2 flops per MAC, D = 64
     flops = sum(p.Hq * 2 * 2 * p.D * L * (L + 1) // 2 for L in qlens)
     tflops = flops / (us * 1e-6) / 1e12
@@ -170,7 +181,13 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step():
+    def fused_step():
+        for layer in range(LAYERS):
+            pkv.paged_attention_decode_append(outs[layer], q, k_layers[layer], v_layers[layer],
+                                              k_new, v_new, tables, lens, case.scale, max_ctx,
+                                              args.partition, ws)
+
+    def two_call_step():
         for layer in range(LAYERS):
             pkv.kv_append(k_layers[layer], v_layers[layer], k_new, v_new, tables, lens)
             pkv.paged_attention_decode(outs[layer], q, k_layers[layer], v_layers[layer], tables,
@@ -181,49 +198,64 @@ def main():
             pkv.paged_attention_decode(outs[layer], q, k_layers[layer], v_layers[layer], tables,
                                        lens, case.scale, max_ctx, args.partition, ws)
 
-    # Eager warm-up, then capture one step (and the decode calls alone) in HIP
-    # graphs: a step is 32 launches whose host-side submission would otherwise
-    # be slower than the GPU work.
+    step, other = (two_call_step, fused_step) if args.two_calls else (fused_step, two_call_step)
+    # Eager warm-up, then capture the step (and, for comparison, the other
+    # form of the step and the decode calls alone) in HIP graphs: host-side
+    # submission of 16-32 launches would otherwise be slower than the GPU work.
+    # Every step stores the same new rows again, so repeated steps see the
+    # same pools.
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     eager = [o.clone() for o in outs]
-    g_step, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_step):
-        step()
-    with torch.cuda.graph(g_dec):
-        decode_only()
-    g_step.replay()
-    torch.cuda.synchronize()
-    if not all(torch.equal(a, b) for a, b in zip(eager, outs)):
-        raise RuntimeError("graph replay differs from the eager step")
+    graphs = {}
+    for name, fn in (("step", step), ("other", other), ("decode", decode_only)):
+        graphs[name] = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graphs[name]):
+            fn()
+    for name in ("step", "other"):
+        graphs[name].replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, b) for a, b in zip(eager, outs)):
+            raise RuntimeError(f"graph replay ({name}) differs from the eager step")
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        g_step.replay()
+        graphs["step"].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall / args.steps * 1e3
 
-    # decode calls alone, HIP events on the stream the graph runs on
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    g_dec.replay()
-    torch.cuda.synchronize()
-    ev0.record()
-    for _ in range(args.steps):
-        g_dec.replay()
-    ev1.record()
-    torch.cuda.synchronize()
-    decode_us = ev0.elapsed_time(ev1) * 1e3 / (args.steps * LAYERS)
+    def event_us(graph, calls):
+        """Average time per call of a graph's calls, HIP events on the stream
+        the graph replays on."""
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / (args.steps * calls)
 
+    decode_us = event_us(graphs["decode"], LAYERS)
+    other_ms = event_us(graphs["other"], 1) * 1e-3
     lens_list = case.context_lens.tolist()
     dec_b = decode_bytes(lens_list, B, Hq, Hkv, D, 2)
     step_b = LAYERS * (dec_b + append_bytes(B, Hkv, D))
     value = step_b / (ms_per_step * 1e-3) / 1e9
-    achieved = dec_b / (decode_us * 1e-6) / 1e9
+    if args.two_calls:
+        kernel = "decode_auto_kernel<false> (paged_attention_decode, one launch per layer)"
+        kernel_us, kernel_b = decode_us, dec_b
+    else:
+        kernel = ("decode_auto_kernel<true> (paged_attention_decode_append, one launch per "
+                  "layer)")
+        kernel_us, kernel_b = event_us(graphs["step"], LAYERS), dec_b + append_bytes(B, Hkv, D)
+    achieved = kernel_b / (kernel_us * 1e-6) / 1e9
     khash = source_hash("decode.hip")
-    traffic = traffic_from_profiles(khash)
+    traffic = traffic_from_profiles(khash, not args.two_calls)
 
     result = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) and seq-tokens/s",
@@ -241,16 +273,21 @@ def main():
         "config": {"workload": "ragged continuous-batching decode: batch 64, context "
                                "log-uniform [16, 8192], 32q/8kv heads, head_dim 64, "
                                "block_size 16, 65536-block pool per layer, 16 layers per step "
-                               "(kv_append + decode each)",
+                               + ("(kv_append + decode each)" if args.two_calls else
+                                  "(one combined append + decode call each)"),
                    "batch": B, "layers": LAYERS, "context_tokens": sum(lens_list),
                    "max_context": max_ctx, "partition_size": args.partition},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "seq_tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_auto_kernel (one launch per paged_attention_decode call)",
-                     "us_per_call": round(decode_us, 2), "algorithmic_bytes": dec_b,
+                     "traffic": traffic, "kernel": kernel,
+                     "us_per_call": round(kernel_us, 2), "algorithmic_bytes": kernel_b,
                      "kernel_source_hash": khash},
+        "other_step_form": {"form": "one combined call per layer" if args.two_calls else
+                            "kv_append + paged_attention_decode per layer",
+                            "ms_per_step": round(other_ms, 4)},
+        "decode_only_us_per_call": round(decode_us, 2),
     }
 
     if not args.no_prefill:

@@ -152,6 +152,35 @@ PKV_API int paged_attention_decode(void *out, int32_t out_dtype, const void *q,
                            int32_t partition_size, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/* paged_attention_decode_append -- one decode step of a layer: store one new
+ * token per sequence in the pools (kv_append with cu_new_lens = NULL), then
+ * attend (paged_attention_decode), with the same results as those two calls.
+ *
+ * Defined by: the two calls it combines (README table of contents "Why KV
+ * cache exists", "Paged KV cache", "Paged Attention"; guide ch. 3, ch. 6: a
+ * decode step caches the new token's K/V and reads the whole cache).
+ *
+ * k_new/v_new   [B][Hkv][D] bf16: the new token of each sequence, which is
+ *               the last of its context_lens[b] tokens.
+ * Other arguments as for paged_attention_decode; k_cache/v_cache are written.
+ * With PKV_PARTITION_AUTO this is one kernel launch: the wavefront that reads
+ * a sequence's last block writes the new rows and uses them directly.  Other
+ * partition sizes run the append and the decode kernels in turn.  Rows are
+ * stored exactly where kv_append stores them (none for context_lens[b] < 1 or
+ * a slot outside the table or pool); the decode is clamped to
+ * max_context_len as in paged_attention_decode.  k_new/v_new must be 16-byte
+ * aligned and must not overlap the pools.
+ */
+PKV_API int paged_attention_decode_append(void *out, int32_t out_dtype, const void *q,
+                                  void *k_cache, void *v_cache,
+                                  const void *k_new, const void *v_new,
+                                  const int32_t *block_tables, const int32_t *context_lens,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t block_size, int32_t max_blocks_per_seq,
+                                  int32_t num_blocks, int32_t max_context_len, float scale,
+                                  int32_t partition_size, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
 /* paged_attention_prefill_causal -- every prompt token attends to the cached
  * tokens up to and including its own position.
  *

@@ -11,6 +11,9 @@ Entry points (same names as the C ABI in include/pagedkv.h):
     paged_attention_decode(out, q, k_cache, v_cache, block_tables,
               context_lens, scale, max_context_len, partition_size=AUTO,
               workspace=None)
+    paged_attention_decode_append(out, q, k_cache, v_cache, k_new, v_new,
+              block_tables, context_lens, scale, max_context_len,
+              partition_size=AUTO, workspace=None)
     paged_attention_prefill_causal(out, q, k_cache, v_cache, block_tables,
               context_lens, cu_q_lens, scale, max_q_len)
     paged_attention_decode_workspace_size(...)
@@ -32,7 +35,8 @@ PARTITION_AUTO = -1
 
 # every symbol include/pagedkv.h declares
 ABI_SYMBOLS = ("pagedkv_last_error", "kv_append", "paged_attention_decode_workspace_size",
-               "paged_attention_decode", "paged_attention_prefill_causal")
+               "paged_attention_decode", "paged_attention_decode_append",
+               "paged_attention_prefill_causal")
 
 _lib = None
 
@@ -62,6 +66,9 @@ def load_library():
     lib.paged_attention_decode.argtypes = [P, I, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I,
                                            P, Z, P]
     lib.paged_attention_decode.restype = ctypes.c_int
+    lib.paged_attention_decode_append.argtypes = [P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
+                                                  I, F, I, P, Z, P]
+    lib.paged_attention_decode_append.restype = ctypes.c_int
     lib.paged_attention_prefill_causal.argtypes = [P, I, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                    I, I, F, P]
     lib.paged_attention_prefill_causal.restype = ctypes.c_int
@@ -157,6 +164,32 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     _check(load_library().paged_attention_decode(
         _dev(out, out.dtype, "out"), _out_dtype(out), _dev(q, torch.bfloat16, "q"),
         _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
+        _dev(block_tables, torch.int32, "block_tables"),
+        _dev(context_lens, torch.int32, "context_lens"), B, Hq, Hkv, D, bs, maxb, N,
+        int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes, _stream()))
+
+
+def paged_attention_decode_append(out, q, k_cache, v_cache, k_new, v_new, block_tables,
+                                  context_lens, scale, max_context_len,
+                                  partition_size=PARTITION_AUTO, workspace=None):
+    """kv_append of one new token per sequence (k_new/v_new [B][Hkv][D]) followed by
+    paged_attention_decode, in one launch for PARTITION_AUTO."""
+    torch = _torch()
+    B, Hq, D = q.shape
+    N, Hkv, bs, _ = k_cache.shape
+    maxb = block_tables.shape[1]
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B][Hq][D]")
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new and v_new must be [B][Hkv][D]")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
+    _check(load_library().paged_attention_decode_append(
+        _dev(out, out.dtype, "out"), _out_dtype(out), _dev(q, torch.bfloat16, "q"),
+        _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
+        _dev(k_new, torch.bfloat16, "k_new"), _dev(v_new, torch.bfloat16, "v_new"),
         _dev(block_tables, torch.int32, "block_tables"),
         _dev(context_lens, torch.int32, "context_lens"), B, Hq, Hkv, D, bs, maxb, N,
         int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes, _stream()))

@@ -130,16 +130,23 @@ size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv,
   return plan.bytes;
 }
 
-int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,
-                           const void* v_cache, const int32_t* block_tables,
-                           const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
-                           int32_t D, int32_t block_size, int32_t max_blocks_per_seq,
-                           int32_t num_blocks, int32_t max_context_len, float scale,
-                           int32_t partition_size, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the decode entry points: fills `a` (the launch
+// arguments) and returns PKV_OK, or returns a status with the error text set.
+// *nothing becomes true when B == 0 (nothing to launch).
+int prepare_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                   const void* v_cache, const int32_t* block_tables,
+                   const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                   int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                   int32_t max_context_len, float scale, int32_t partition_size,
+                   void* workspace, size_t workspace_bytes, pkv::DecodeArgs* a, bool* nothing) {
   DecodePlan plan;
   int rc = plan_decode(B, Hq, Hkv, D, block_size, max_context_len, partition_size, &plan);
   if (rc != PKV_OK) return rc;
+  *nothing = B == 0;
   if (B == 0) return PKV_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
@@ -158,31 +165,88 @@ int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const vo
   }
   if ((int64_t)B * Hkv * plan.parts_max / 4 >= INT32_MAX)
     return fail(PKV_ERR_UNSUPPORTED, "too many (sequence, head, partition) units for one launch");
-  pkv::DecodeArgs a;
-  a.out = out;
-  a.out_f32 = out_dtype == PKV_OUT_F32;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.B = B;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.num_blocks = num_blocks;
-  a.max_context_len = max_context_len;
-  a.scale = scale;
-  a.mode = plan.mode;
-  a.part_blocks = plan.part_blocks;
-  a.parts_max = plan.parts_max;
+  *a = pkv::DecodeArgs{};
+  a->out = out;
+  a->out_f32 = out_dtype == PKV_OUT_F32;
+  a->q = q;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->block_tables = block_tables;
+  a->context_lens = context_lens;
+  a->B = B;
+  a->Hq = Hq;
+  a->Hkv = Hkv;
+  a->max_blocks_per_seq = max_blocks_per_seq;
+  a->num_blocks = num_blocks;
+  a->max_context_len = max_context_len;
+  a->scale = scale;
+  a->mode = plan.mode;
+  a->part_blocks = plan.part_blocks;
+  a->parts_max = plan.parts_max;
   float* rec = plan.bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
                                                      pkv::kCounterBytes)
                          : nullptr;
-  a.ws_count = plan.bytes ? static_cast<uint32_t*>(workspace) : nullptr;
-  a.ws_o = rec;
-  a.ws_ml = plan.bytes ? rec + plan.records * pkv::kRecordFloats : nullptr;
+  a->ws_count = plan.bytes ? static_cast<uint32_t*>(workspace) : nullptr;
+  a->ws_o = rec;
+  a->ws_ml = plan.bytes ? rec + plan.records * pkv::kRecordFloats : nullptr;
+  a->k_new = nullptr;
+  a->v_new = nullptr;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,
+                           const void* v_cache, const int32_t* block_tables,
+                           const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv,
+                           int32_t D, int32_t block_size, int32_t max_blocks_per_seq,
+                           int32_t num_blocks, int32_t max_context_len, float scale,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  pkv::DecodeArgs a;
+  bool nothing = false;
+  const int rc = prepare_decode(out, out_dtype, q, k_cache, v_cache, block_tables, context_lens, B,
+                                Hq, Hkv, D, block_size, max_blocks_per_seq, num_blocks,
+                                max_context_len, scale, partition_size, workspace,
+                                workspace_bytes, &a, &nothing);
+  if (rc != PKV_OK || nothing) return rc;
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream), "paged_attention_decode launch");
+}
+
+int paged_attention_decode_append(void* out, int32_t out_dtype, const void* q, void* k_cache,
+                                  void* v_cache, const void* k_new, const void* v_new,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t block_size, int32_t max_blocks_per_seq,
+                                  int32_t num_blocks, int32_t max_context_len, float scale,
+                                  int32_t partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  pkv::DecodeArgs a;
+  bool nothing = false;
+  const int rc = prepare_decode(out, out_dtype, q, k_cache, v_cache, block_tables, context_lens, B,
+                                Hq, Hkv, D, block_size, max_blocks_per_seq, num_blocks,
+                                max_context_len, scale, partition_size, workspace,
+                                workspace_bytes, &a, &nothing);
+  if (rc != PKV_OK || nothing) return rc;
+  if (!k_new || !v_new) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(k_new) || !aligned16(v_new))
+    return fail(PKV_ERR_INVALID_ARG, "new rows must be 16-byte aligned");
+  if (a.mode == pkv::kAuto) {  // one launch: the decode kernel stores the new rows
+    a.k_new = k_new;
+    a.v_new = v_new;
+    return hip_status(pkv::launch_decode(a, (hipStream_t)stream),
+                      "paged_attention_decode_append launch");
+  }
+  // other partition modes: the append kernel, then the decode kernel
+  pkv::KvAppendArgs ap{k_cache, v_cache, k_new, v_new, block_tables, context_lens, nullptr,
+                       B, B, Hkv, D, block_size, max_blocks_per_seq, num_blocks};
+  const int rc2 = hip_status(pkv::launch_kv_append(ap, (hipStream_t)stream),
+                             "paged_attention_decode_append launch (append)");
+  if (rc2 != PKV_OK) return rc2;
+  return hip_status(pkv::launch_decode(a, (hipStream_t)stream),
+                    "paged_attention_decode_append launch (decode)");
 }
 
 int paged_attention_prefill_causal(void* out, int32_t out_dtype, const void* q,

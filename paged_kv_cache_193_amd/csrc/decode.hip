@@ -83,6 +83,8 @@ struct Params {
   float* ws_ml;
   uint32_t* ws_count;  // per stream (b, g): split records written so far
   int n_records;       // records in ws_o / ws_ml
+  const uint16_t* k_new;  // append variant: the new token's K / V rows [B][Hkv][D]
+  const uint16_t* v_new;
 };
 
 // Split records are written and read with 16-byte buffer accesses at agent
@@ -708,6 +710,14 @@ __device__ __forceinline__ void load_q(uint32_t (&qv)[4][4], const Params& p, in
   }
 }
 
+// Append variant: chunk i of the new token's K and V rows of stream (b, g).
+__device__ __forceinline__ void load_new(u32x4& kn, u32x4& vn, const Params& p, int b, int g,
+                                         int i) {
+  const int64_t off = ((int64_t)b * p.Hkv + g) * kD + 8 * i;
+  kn = *reinterpret_cast<const u32x4*>(p.k_new + off);
+  vn = *reinterpret_cast<const u32x4*>(p.v_new + off);
+}
+
 __device__ __forceinline__ void reset_state(LaneState& st) {
   st.m = -INFINITY;
   st.l = 0.f;
@@ -717,12 +727,22 @@ __device__ __forceinline__ void reset_state(LaneState& st) {
     for (int e = 0; e < 8; ++e) st.acc[j][e] = 0.f;
 }
 
+//
+// kAppend: the call also stores one new token per sequence (kv_append with
+// one token each).  The new token is the last of its sequence, so it lies in
+// the stream's last block, which exactly one wavefront consumes: that
+// wavefront writes the token's K and V rows into the pools and uses them
+// from registers in place of the (stale) rows its load returned.  The rows
+// of a sequence clamped to max_context_len are stored by a workgroup during
+// set-up; slots outside the table or pool are not written (as kv_append).
+template <bool kAppend>
 __global__ void __launch_bounds__(kWaves * 64)
 decode_auto_kernel(Params p) {
   __shared__ float red[kWaves][8 * 4 * kD];
   __shared__ int pfx[kAutoMaxBatch + 1];
   __shared__ int s_ctx[kAutoMaxBatch];
   __shared__ int wsum[kWaves];
+  __shared__ unsigned char s_newok[kAppend ? kAutoMaxBatch : 1];  // append this sequence
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -735,6 +755,7 @@ decode_auto_kernel(Params p) {
   for (int k = beg; k < end; ++k) {
     const int c = eff_ctx(p, k);
     s_ctx[k] = c;
+    if (kAppend) s_newok[k] = c >= 1 && c == p.context_lens[k];
     local += padded_blocks(c);
   }
   int incl = local;
@@ -771,6 +792,25 @@ decode_auto_kernel(Params p) {
         else reinterpret_cast<uint16_t*>(p.out)[idx] = 0;
       }
     }
+    // a sequence cut short by the clamp still gets its token stored (no
+    // wavefront reads that row): workgroup k % grid copies it
+    if (kAppend && !s_newok[k]) {
+      const int len = p.context_lens[k];
+      if (len >= 1 && len <= p.max_blocks * kBS) {
+        const int pos = len - 1;
+        const int id = p.block_tables[(int64_t)k * p.max_blocks + pos / kBS];
+        if (id >= 0 && id < p.num_blocks) {
+          for (int e = tid; e < p.Hkv * (kD / 8); e += kWaves * 64) {
+            const int g = e / (kD / 8), ch = e % (kD / 8);
+            u32x4 kn, vn;
+            load_new(kn, vn, p, k, g, ch);
+            const int64_t off = (((int64_t)id * p.Hkv + g) * kBS + pos % kBS) * kD + 8 * ch;
+            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_cache) + off) = kn;
+            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_cache) + off) = vn;
+          }
+        }
+      }
+    }
   }
   const int w = blockIdx.x * kWaves + wave;
   const int64_t x0 = share_start(w, gbase, rem);
@@ -804,14 +844,22 @@ decode_auto_kernel(Params p) {
   int tab = id_window(p, s_ctx, ci, x0, x1, lane);
   BlockRegs ring[kRing];
   int nvalid[kRing];
+  bool slast[kRing];  // append: the slot holds its stream's last block
+  int sphys[kRing];   // append: that block's physical id
   uint32_t qv[4][4], qn[4][4];
+  u32x4 knv, vnv, knn, vnn;  // append: new-token chunks (consumed / next group)
   load_q(qn, p, ci.b, ci.g, i, c);
+  if (kAppend) load_new(knn, vnn, p, ci.b, ci.g, i);
 #pragma unroll
   for (int s = 0; s < kRing; ++s) {
     const int j = ci.j + s < ci.nbr - 1 ? ci.j + s : ci.nbr - 1;
     const int id = __builtin_amdgcn_readlane(tab, (int)(xi - win) + s);
     const int nv = issue_block(ring[s], p, id, ci.g, j, ci.ctx, lane_off);
     nvalid[s] = ci.j + s < ci.nbr ? nv : 0;
+    if (kAppend) {
+      slast[s] = ci.j + s == ci.nbr - 1 && nv > 0;
+      sphys[s] = id;
+    }
   }
   if (xi + kRing < x1) {
     xi += kRing;
@@ -839,6 +887,31 @@ decode_auto_kernel(Params p) {
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int w2 = 0; w2 < 4; ++w2) qv[j][w2] = qn[j][w2];
+    if (kAppend) {
+      knv = knn;
+      vnv = vnn;
+      // the new token's row replaces the one loaded from the pools, and is
+      // stored there (lanes grp == t % 8 hold token t in ka/va or kb/vb)
+#pragma unroll
+      for (int s = 0; s < kRing; ++s) {
+        if (slast[s] && s_newok[cc.b]) {
+          const int t = (cc.ctx - 1) & (kBS - 1);
+          if (grp == t) {
+            ring[s].ka = knv;
+            ring[s].va = vnv;
+          }
+          if (grp + 8 == t) {
+            ring[s].kb = knv;
+            ring[s].vb = vnv;
+          }
+          if (grp == (t & 7)) {
+            const int64_t off = (((int64_t)sphys[s] * p.Hkv + cc.g) * kBS + t) * kD + 8 * i;
+            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_cache) + off) = knv;
+            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_cache) + off) = vnv;
+          }
+        }
+      }
+    }
 
     bool full = true;
 #pragma unroll
@@ -880,7 +953,14 @@ decode_auto_kernel(Params p) {
       const int id = __builtin_amdgcn_readlane(tab, (int)(xr - win) + s);
       const int nv = issue_block(ring[s], p, id, ci.g, j, ci.ctx, lane_off);
       nvalid[s] = ci.j + s < ci.nbr ? nv : 0;
-      if (s == 0) load_q(qn, p, ci.b, ci.g, i, c);
+      if (kAppend) {
+        slast[s] = ci.j + s == ci.nbr - 1 && nv > 0;
+        sphys[s] = id;
+      }
+      if (s == 0) {
+        load_q(qn, p, ci.b, ci.g, i, c);
+        if (kAppend) load_new(knn, vnn, p, ci.b, ci.g, i);
+      }
     }
     if (xi + kRing < x1) {
       xi += kRing;
@@ -974,6 +1054,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.ws_ml = a.ws_ml;
   p.ws_count = a.ws_count;
   p.n_records = (int)decode_records(a.mode, a.B, a.Hkv, a.parts_max);
+  p.k_new = (const uint16_t*)a.k_new;
+  p.v_new = (const uint16_t*)a.v_new;
   const int streams = a.B * a.Hkv;
   if (a.mode == kWhole) {
     const int grid = (streams + kWaves - 1) / kWaves;
@@ -983,8 +1065,12 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     const int grid = (int)((units + kWaves - 1) / kWaves);
     hipLaunchKernelGGL(decode_units_kernel<kFixed>, dim3(grid), dim3(kWaves * 64), 0, stream, p);
   } else {
-    hipLaunchKernelGGL(decode_auto_kernel, dim3(kAutoWaves / kWaves), dim3(kWaves * 64), 0,
-                       stream, p);
+    if (a.k_new)
+      hipLaunchKernelGGL(decode_auto_kernel<true>, dim3(kAutoWaves / kWaves), dim3(kWaves * 64),
+                         0, stream, p);
+    else
+      hipLaunchKernelGGL(decode_auto_kernel<false>, dim3(kAutoWaves / kWaves), dim3(kWaves * 64),
+                         0, stream, p);
   }
   return hipGetLastError();
 }

@@ -59,6 +59,10 @@ struct DecodeArgs {
   float* ws_o;             // records x kRecordFloats
   float* ws_ml;            // records x 4 heads x (m, l)
   uint32_t* ws_count;      // B x Hkv split counters, zero between calls
+  // kAuto only: also store one new token per sequence ([B][Hkv][D] rows)
+  // into the pools before attending (both null: plain decode)
+  const void* k_new;
+  const void* v_new;
 };
 size_t decode_records(int32_t mode, int32_t B, int32_t Hkv, int32_t parts_max);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -103,6 +103,39 @@ def test_decode_workspace_size(lib):
     assert ws(8, 32, 8, 128, 16, 2048, 512) == 0          # rejected -> 0
 
 
+def decode_append_call(lib, **kw):
+    a = dict(out=FAKE, out_dtype=pkv.PKV_OUT_F32, q=FAKE, k=FAKE, v=FAKE, kn=FAKE, vn=FAKE,
+             bt=FAKE, cl=FAKE, B=2, Hq=32, Hkv=8, D=64, bs=16, maxb=4, N=8, maxctx=64,
+             scale=0.125, part=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.paged_attention_decode_append(
+        a["out"], a["out_dtype"], a["q"], a["k"], a["v"], a["kn"], a["vn"], a["bt"], a["cl"],
+        a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["maxb"], a["N"], a["maxctx"], a["scale"],
+        a["part"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(D=128), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(Hq=16, Hkv=8), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(kn=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(vn=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(kn=ctypes.c_void_p(0x1004)), pkv.PKV_ERR_INVALID_ARG),
+    (dict(k=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), pkv.PKV_ERR_INVALID_ARG),
+    (dict(part=-1), pkv.PKV_ERR_WORKSPACE),
+    (dict(part=-1, B=5000), pkv.PKV_ERR_UNSUPPORTED),
+])
+def test_decode_append_rejects(lib, kw, code):
+    assert decode_append_call(lib, **kw) == code
+    assert pkv.last_error()
+
+
+def test_decode_append_empty_batch_is_a_noop(lib):
+    assert decode_append_call(lib, B=0, out=None, q=None, k=None, v=None, kn=None, vn=None,
+                              bt=None, cl=None) == pkv.PKV_OK
+
+
 def append_call(lib, **kw):
     a = dict(k=FAKE, v=FAKE, kn=FAKE, vn=FAKE, bt=FAKE, cl=FAKE, cu=None, B=2, T=2, Hkv=8, D=64,
              bs=16, maxb=4, N=8, stream=None)
