@@ -110,9 +110,7 @@ def cpu_baseline(case, k_layers, v_layers, min_seconds=10.0):
 
 
 def run_prefill(torch, pkv, wl, steps, warmup):
-    """Causal paged prefill of 4 x 512 + 2 x 2048 prompts, in both launch
-    forms (split form with a workspace, and one workgroup per query tile);
-    returns a dict whose roofline is the split form's."""
+    """Causal paged prefill of 4 x 512 + 2 x 2048 prompts; returns a dict."""
     dev = "cuda"
     p = wl.prefill_case()
     k, v = p.k_cache.to(dev), p.v_cache.to(dev)
@@ -122,46 +120,31 @@ def run_prefill(torch, pkv, wl, steps, warmup):
     out = torch.empty(tuple(p.q.shape), dtype=torch.bfloat16, device=dev)
     qlens = (p.cu_q_lens[1:] - p.cu_q_lens[:-1]).tolist()
     maxq = max(qlens)
-    ws = pkv.prefill_workspace(p.B, int(p.q.shape[0]), p.Hq, p.Hkv, p.D, 16, dev)
-
-    def time_form(workspace):
-        for _ in range(warmup):
-            pkv.paged_attention_prefill_causal(out, q, k, v, t, l, cu, p.scale, maxq, workspace)
-        torch.cuda.synchronize()
-        # several calls per graph, so the gap between graph replays is not
-        # counted as kernel time
-        per_graph = 8
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(per_graph):
-                pkv.paged_attention_prefill_causal(out, q, k, v, t, l, cu, p.scale, maxq,
-                                                   workspace)
+    for _ in range(warmup):
+        pkv.paged_attention_prefill_causal(out, q, k, v, t, l, cu, p.scale, maxq)
+    torch.cuda.synchronize()
+    # several calls per graph, so the gap between graph replays is not
+    # counted as kernel time
+    per_graph = 8
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            pkv.paged_attention_prefill_causal(out, q, k, v, t, l, cu, p.scale, maxq)
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
         graph.replay()
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
-        for _ in range(steps):
-            graph.replay()
-        ev1.record()
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) / (steps * per_graph) * 1e3
-
-    us_tile = time_form(None)
-    us_split = time_form(ws)
-    # the faster launch form is the one reported (and the one a caller uses)
-    split_faster = us_split < us_tile
-    us = us_split if split_faster else us_tile
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) / (steps * per_graph) * 1e3
     # visible (query, key) pairs: QK^T and PV, 2 flops per MAC, D = 64
     flops = sum(p.Hq * 2 * 2 * p.D * L * (L + 1) // 2 for L in qlens)
     tflops = flops / (us * 1e-6) / 1e12
     return {"workload": "causal paged prefill, prompts 4x512 + 2x2048, 32q/8kv heads, "
                         "head_dim 64, block_size 16, bf16",
-            "kernel": ("prefill_kernel<true> (long query tiles split in two, workspace)"
-                       if split_faster else
-                       "prefill_kernel<false> (one workgroup per query tile, no workspace)"),
             "us_per_call": round(us, 2), "flops": flops,
-            "per_query_tile_form_us_per_call": round(us_tile, 2),
-            "split_form_us_per_call": round(us_split, 2),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}}

@@ -194,18 +194,6 @@ PKV_API int paged_attention_decode_append(void *out, int32_t out_dtype, const vo
  * q             [T_q][Hq][D] bf16, packed by sequence.
  * cu_q_lens     [B+1] int32 prefix sums of query tokens per sequence.
  * max_q_len     host-side upper bound of the per-sequence query counts.
- * workspace     NULL: one workgroup per (64-row query tile, sequence, KV
- *               head); the last query tile of the longest prompt then sets
- *               the kernel's length.  Otherwise device scratch of at least
- *               paged_attention_prefill_workspace_size(B, T_q, ...) bytes:
- *               query tiles that see more than 16 key tiles of 64 keys are
- *               cut into two halves of their key range, one workgroup each,
- *               and the half that finishes second merges both by
- *               log-sum-exp (the result does not depend on which half that
- *               is).  The workspace starts with one counter per (query tile,
- *               KV head), which must be zero before the first use; every
- *               call leaves them zero.  Calls sharing a workspace must not
- *               run concurrently.
  * Other arguments as for decode.  This build implements D == 64,
  * block_size == 16 and Hq == 4 * Hkv.
  */
@@ -217,15 +205,7 @@ PKV_API int paged_attention_prefill_causal(void *out, int32_t out_dtype, const v
                                    int32_t Hq, int32_t Hkv, int32_t D,
                                    int32_t block_size, int32_t max_blocks_per_seq,
                                    int32_t num_blocks, int32_t max_q_len, float scale,
-                                   void *workspace, size_t workspace_bytes, void *stream);
-
-/* Bytes of device workspace the split form of paged_attention_prefill_causal
- * needs: 4-byte counters for (T_q / 64 + B) * Hkv query tiles, 256-byte
- * aligned, then two 68 KiB partial records per counter (about 1.1 MB per 64
- * prompt tokens at Hkv = 8).  0 for arguments the call rejects (B < 1,
- * T_q < 0, D != 64, block_size != 16, Hq != 4 * Hkv).  Makes no HIP call. */
-PKV_API size_t paged_attention_prefill_workspace_size(int32_t B, int32_t T_q, int32_t Hq,
-                                              int32_t Hkv, int32_t D, int32_t block_size);
+                                   void *stream);
 
 #ifdef __cplusplus
 }

@@ -15,9 +15,8 @@ Entry points (same names as the C ABI in include/pagedkv.h):
               block_tables, context_lens, scale, max_context_len,
               partition_size=AUTO, workspace=None)
     paged_attention_prefill_causal(out, q, k_cache, v_cache, block_tables,
-              context_lens, cu_q_lens, scale, max_q_len, workspace=None)
+              context_lens, cu_q_lens, scale, max_q_len)
     paged_attention_decode_workspace_size(...)
-    paged_attention_prefill_workspace_size(...)
 """
 import ctypes
 import os
@@ -37,7 +36,7 @@ PARTITION_AUTO = -1
 # every symbol include/pagedkv.h declares
 ABI_SYMBOLS = ("pagedkv_last_error", "kv_append", "paged_attention_decode_workspace_size",
                "paged_attention_decode", "paged_attention_decode_append",
-               "paged_attention_prefill_causal", "paged_attention_prefill_workspace_size")
+               "paged_attention_prefill_causal")
 
 _lib = None
 
@@ -71,10 +70,8 @@ def load_library():
                                                   I, F, I, P, Z, P]
     lib.paged_attention_decode_append.restype = ctypes.c_int
     lib.paged_attention_prefill_causal.argtypes = [P, I, P, P, P, P, P, P, I, I, I, I, I, I, I,
-                                                   I, I, F, P, Z, P]
+                                                   I, I, F, P]
     lib.paged_attention_prefill_causal.restype = ctypes.c_int
-    lib.paged_attention_prefill_workspace_size.argtypes = [I, I, I, I, I, I]
-    lib.paged_attention_prefill_workspace_size.restype = Z
     _lib = lib
     return lib
 
@@ -198,29 +195,9 @@ def paged_attention_decode_append(out, q, k_cache, v_cache, k_new, v_new, block_
         int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes, _stream()))
 
 
-def paged_attention_prefill_workspace_size(B, T_q, Hq, Hkv, D, block_size) -> int:
-    return int(load_library().paged_attention_prefill_workspace_size(B, T_q, Hq, Hkv, D,
-                                                                     block_size))
-
-
-def prefill_workspace(B, T_q, Hq, Hkv, D, block_size, device):
-    """Allocate (with torch) the zero-filled workspace of the split prefill
-    form for batches of up to B sequences and T_q query tokens, or None when
-    the arguments do not allow it.  Calls leave its counters zero, so it can
-    be reused call after call."""
-    n = paged_attention_prefill_workspace_size(B, T_q, Hq, Hkv, D, block_size)
-    if n == 0:
-        return None
-    return _torch().zeros(n, dtype=_torch().uint8, device=device)
-
-
 def paged_attention_prefill_causal(out, q, k_cache, v_cache, block_tables, context_lens,
-                                   cu_q_lens, scale, max_q_len, workspace=None):
-    """out[T][Hq][D] = causal paged prefill attention of packed q[T][Hq][D].
-
-    workspace: None (one workgroup per query tile) or a device uint8 tensor of
-    at least paged_attention_prefill_workspace_size(B, T, ...) bytes (long
-    query tiles split in two halves)."""
+                                   cu_q_lens, scale, max_q_len):
+    """out[T][Hq][D] = causal paged prefill attention of packed q[T][Hq][D]."""
     torch = _torch()
     T, Hq, D = q.shape
     N, Hkv, bs, _ = k_cache.shape
@@ -229,17 +206,13 @@ def paged_attention_prefill_causal(out, q, k_cache, v_cache, block_tables, conte
         raise ValueError("out must be [T][Hq][D]")
     if cu_q_lens.numel() != B + 1:
         raise ValueError("cu_q_lens must have B+1 entries")
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        ws_ptr = _dev(workspace, torch.uint8, "workspace")
-        ws_bytes = workspace.numel()
     _check(load_library().paged_attention_prefill_causal(
         _dev(out, out.dtype, "out"), _out_dtype(out), _dev(q, torch.bfloat16, "q"),
         _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
         _dev(block_tables, torch.int32, "block_tables"),
         _dev(context_lens, torch.int32, "context_lens"),
         _dev(cu_q_lens, torch.int32, "cu_q_lens"), B, T, Hq, Hkv, D, bs, maxb, N,
-        int(max_q_len), float(scale), ws_ptr, ws_bytes, _stream()))
+        int(max_q_len), float(scale), _stream()))
 
 
 def decode_workspace(B, Hq, Hkv, D, block_size, max_context_len, partition_size, device):

@@ -121,15 +121,6 @@ int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new
   return hip_status(pkv::launch_kv_append(a, (hipStream_t)stream), "kv_append launch");
 }
 
-size_t paged_attention_prefill_workspace_size(int32_t B, int32_t T_q, int32_t Hq, int32_t Hkv,
-                                              int32_t D, int32_t block_size) {
-  if (B <= 0 || T_q < 0 || Hkv <= 0 || Hq != kGroup * Hkv || D != kD || block_size != kBS)
-    return 0;
-  const pkv::PrefillSplitLayout ly = pkv::prefill_split_layout(B, T_q, Hkv);
-  if (ly.counters * 2 > (size_t)INT32_MAX) return 0;
-  return ly.bytes;
-}
-
 size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                              int32_t block_size, int32_t max_context_len,
                                              int32_t partition_size) {
@@ -264,8 +255,7 @@ int paged_attention_prefill_causal(void* out, int32_t out_dtype, const void* q,
                                    const int32_t* cu_q_lens, int32_t B, int32_t T_q, int32_t Hq,
                                    int32_t Hkv, int32_t D, int32_t block_size,
                                    int32_t max_blocks_per_seq, int32_t num_blocks,
-                                   int32_t max_q_len, float scale, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+                                   int32_t max_q_len, float scale, void* stream) {
   if (B < 0 || T_q < 0)
     return fail(PKV_ERR_INVALID_ARG, "B (%d) and T_q (%d) must be >= 0", B, T_q);
   if (Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0)
@@ -286,19 +276,6 @@ int paged_attention_prefill_causal(void* out, int32_t out_dtype, const void* q,
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_ERR_INVALID_ARG, "out, q and the pools must be 16-byte aligned");
-  const int64_t q_tiles = ((int64_t)max_q_len + 63) / 64;
-  if (q_tiles * B * Hkv * 2 > INT32_MAX)
-    return fail(PKV_ERR_UNSUPPORTED, "too many (query tile, sequence, head) units for one launch");
-  if (workspace) {
-    // records are numbered with int32: 2 per (query tile, KV head)
-    const pkv::PrefillSplitLayout ly = pkv::prefill_split_layout(B, T_q, Hkv);
-    if (ly.counters * 2 > (size_t)INT32_MAX)
-      return fail(PKV_ERR_UNSUPPORTED, "prefill too large for the split form: pass no workspace");
-    if (workspace_bytes < ly.bytes)
-      return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ly.bytes,
-                  workspace_bytes);
-    if (!aligned16(workspace)) return fail(PKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-  }
   pkv::PrefillArgs a;
   a.out = out;
   a.out_f32 = out_dtype == PKV_OUT_F32;
@@ -316,7 +293,6 @@ int paged_attention_prefill_causal(void* out, int32_t out_dtype, const void* q,
   a.num_blocks = num_blocks;
   a.max_q_len = max_q_len;
   a.scale = scale;
-  a.workspace = workspace;
   return hip_status(pkv::launch_prefill(a, (hipStream_t)stream),
                     "paged_attention_prefill_causal launch");
 }

@@ -78,25 +78,7 @@ struct PrefillArgs {
   const int32_t* cu_q_lens;
   int32_t B, T_q, Hq, Hkv, max_blocks_per_seq, num_blocks, max_q_len;
   float scale;
-  void* workspace;  // null: one workgroup per query tile; else the balanced split
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
-
-// Split prefill workspace: one counter per (query tile, KV head) and two
-// records per counter.  Query tile t of sequence b has the batch-wide index
-// cu_q_lens[b] / 64 + b + t < T_q / 64 + B.
-constexpr int kPrefillRecordOBytes = 65536;  // 4 heads x 64 rows x 64 d fp32
-constexpr int kPrefillRecordMLBytes = 4096;  // 4 heads x 2 x 64 lanes x (m, l) fp32
-struct PrefillSplitLayout {
-  size_t counters, o_offset, ml_offset, bytes;
-};
-inline PrefillSplitLayout prefill_split_layout(int32_t B, int32_t T_q, int32_t Hkv) {
-  PrefillSplitLayout ly;
-  ly.counters = ((size_t)T_q / 64 + (size_t)B) * (size_t)Hkv;
-  ly.o_offset = (ly.counters * 4 + 255) / 256 * 256;
-  ly.ml_offset = ly.o_offset + 2 * ly.counters * kPrefillRecordOBytes;
-  ly.bytes = ly.ml_offset + 2 * ly.counters * kPrefillRecordMLBytes;
-  return ly;
-}
 
 }  // namespace pkv

@@ -36,19 +36,9 @@
 // Causal rule: query row t of a prompt of q_len tokens whose sequence holds
 // context_len tokens sits at position context_len - q_len + t and sees keys
 // 0..pos.  Key tiles entirely below the first row's position need no mask;
-// only diagonal tiles are masked.
-//
-// Two launch forms:
-//  - prefill_kernel (no workspace): one workgroup per (query tile, sequence,
-//    KV group), heaviest query tiles first, KV group fastest varying.  The
-//    last query tile of a long prompt walks every key tile of the prompt, so
-//    it sets the kernel's length.
-//  - split form (with a workspace): the same grid with every query tile that
-//    sees more than kSplitTiles key tiles cut into two halves of its key
-//    range, one workgroup each, so the longest unit is about half as long.
-//    Each half writes a record (unnormalised O, m, l); the half that finishes
-//    second merges both by log-sum-exp, writes the rows and re-zeroes the
-//    counter.
+// only diagonal tiles are masked.  Query tiles are launched heaviest first
+// and the KV group is the fastest-varying grid index (one KV head per XCD's
+// L2 for the 8-head case).
 #include "device_common.h"
 #include "launch.h"
 
@@ -68,8 +58,6 @@ constexpr int kVRow = kTile + 4;   // V^T tile row stride (bf16 elements): 136 b
 // sends the tile through the exact-max path.  Weights stay below 2^10.
 constexpr float kLazyBound = 1024.f;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 pair (1, 1)
-// split form: query tiles that see more key tiles than this are cut in two
-constexpr int kSplitTiles = 16;
 
 struct PParams {
   void* out;
@@ -83,23 +71,7 @@ struct PParams {
   int B, Hq, Hkv, max_blocks, num_blocks, tiles_max;
   float c_log2;     // |scale| * log2(e), floored at 1e-30: scores to log2 units
   uint32_t q_sign;  // 0x80008000 when scale < 0 (q is negated), else 0
-  // split form only
-  float* ws_o;          // records: [record][wave][16][lane] f32x4, unnormalised O
-  float* ws_ml;         // records: [record][wave][qt][lane] (m, l)
-  uint32_t* ws_count;   // per (split query tile, KV group): halves finished
 };
-
-// Split records are written and read with 16-byte buffer accesses at agent
-// scope (sc1), so a piece written on one XCD is seen by a workgroup merging on
-// another; the descriptors also bound every access to the records.
-constexpr int kSc1 = 16;
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, dword data
-constexpr int kRecOBytes = kPrefillRecordOBytes;    // 4 waves x 16 f32x4 x 64 lanes
-constexpr int kRecMLBytes = kPrefillRecordMLBytes;  // 4 waves x 2 column sets x 64 lanes x (m, l)
-static_assert(kRecOBytes == 4 * 16 * 64 * 16 && kRecMLBytes == 4 * 2 * 64 * 8,
-              "record layout");
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr f32x16 kZero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f,
                              0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -162,33 +134,42 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* ks, uint
   }
 }
 
-// Softmax and accumulator state of one wavefront's 64 query columns.
-struct QTileState {
-  f32x16 o[2][2];   // O^T [dt][qt], unnormalised (weights against m_ref)
-  float m_ref[2];   // reference max per column, log2 units
-  float l_run[2];   // this lane's share of the row sum
-  bool has_ref[2];  // false until the column has seen a visible key
-};
+__global__ void __launch_bounds__(256, 2)
+prefill_kernel(PParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t ks_buf[2][kTile * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_buf[2][kD * kVRow];
+  __shared__ u32x4 qs_buf[4][2 * 4 * 64];
 
-__device__ __forceinline__ void reset_state(QTileState& st) {
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) st.o[a][c] = kZero16;
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    st.m_ref[qt] = 0.f;
-    st.l_run[qt] = 0.f;
-    st.has_ref[qt] = false;
-  }
-}
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // grid: g fastest, then b, then query tile from the last (heaviest) down
+  const int g = blockIdx.x % p.Hkv;
+  const int rest = blockIdx.x / p.Hkv;
+  const int b = rest % p.B;
+  const int tile = p.tiles_max - 1 - rest / p.B;
 
-// Q^T operand of query rows [q0, q0 + 64) of head h, kept in this wavefront's
-// LDS area: lane holds q row (qt*32 + lane%32), d in [k*16 + 8*(lane/32), +8).
-// Rows past the prompt repeat its last row (their results are not written).
-__device__ __forceinline__ void load_q_operand(u32x4* qsw, const PParams& p, int qs, int q_len,
-                                               int q0, int h, int lane) {
+  const int qs = p.cu_q_lens[b];
+  const int q_len = p.cu_q_lens[b + 1] - qs;
+  const int q0 = tile * kTile;
+  if (q0 >= q_len) return;
+  int ctx = p.context_lens[b];
+  const int cap = p.max_blocks * kBS;
+  ctx = ctx > cap ? cap : ctx;
+  const int hist = ctx - q_len;  // position of query row 0 minus 0
+  const int rows = q_len - q0 < kTile ? q_len - q0 : kTile;
+  const int pos_first = hist + q0;
+  const int pos_last = hist + q0 + rows - 1;
+  int kend = pos_last + 1 < ctx ? pos_last + 1 : ctx;  // keys [0, kend)
+  if (kend < 0) kend = 0;
+  const int n_tiles = (kend + kTile - 1) / kTile;
+  const int h = 4 * g + wave;
+  const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks;
+
+  // Q^T operand, kept in LDS: lane holds q row (qt*32 + lane%32), d in
+  // [k*16 + 8*(lane/32), +8)
   const int lr = lane & 31, lh = lane >> 5;
+  u32x4* qsw = qs_buf[wave];  // this wavefront's Q^T operand [qt][k][lane]
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     int row = q0 + qt * 32 + lr;
@@ -199,34 +180,37 @@ __device__ __forceinline__ void load_q_operand(u32x4* qsw, const PParams& p, int
       qsw[(qt * 4 + k) * 64 + lane] = *reinterpret_cast<const u32x4*>(qr + 16 * k) ^
                                       u32x4{p.q_sign, p.q_sign, p.q_sign, p.q_sign};
   }
-}
 
-// Key tiles [kt_a, kt_b) (kt_b > kt_a) of one query tile, accumulated into
-// st.  K/V tiles go global -> registers -> LDS one tile ahead of the MFMAs,
-// and the block id of the tile after that is read one more tile ahead, so no
-// load waits on a table read.  Ends with a workgroup barrier; the LDS tile
-// buffers are free again afterwards.
-__device__ __forceinline__ void run_key_tiles(QTileState& st, const PParams& p, uint16_t* ks_base,
-                                              uint16_t* vt_base, const u32x4* qsw,
-                                              const int32_t* trow, int g, int ctx, int pos_first,
-                                              int kt_a, int kt_b, int tid, int lane) {
-  const int lr = lane & 31, lh = lane >> 5;
+  f32x16 o[2][2];  // [dt][qt]
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) o[a][c] = kZero16;
+  // Reference max m per query column (log2 units): weights are
+  // exp2(c * s - m).  has_ref is false until the column has seen a visible key.
+  float m_ref[2] = {0.f, 0.f};
+  bool has_ref[2] = {false, false};
   const float c2 = p.c_log2;
+  float l_run[2] = {0.f, 0.f};  // this lane's share of the row sum
+
+  // K/V tiles go global -> registers -> LDS one tile ahead of the MFMAs, and
+  // the block id of the tile after that is read one more tile ahead, so no
+  // load waits on a table read.
   TileRegs nxt;
-  int id_next = tile_block_id(p, trow, (kt_a + 1) * kTile, tid);
-  load_tile(nxt, p, tile_block_id(p, trow, kt_a * kTile, tid), g, ctx, kt_a * kTile, tid);
-  store_tile(nxt, ks_base, vt_base, tid);
+  int id_next = tile_block_id(p, trow, kTile, tid);
+  load_tile(nxt, p, tile_block_id(p, trow, 0, tid), g, ctx, 0, tid);
+  store_tile(nxt, ks_buf[0], vt_buf[0], tid);
   __syncthreads();
 
-  for (int it = kt_a; it < kt_b; ++it) {
+  for (int it = 0; it < n_tiles; ++it) {
     const int k0 = it * kTile;
-    const int buf = (it - kt_a) & 1;
+    const int buf = it & 1;
     // past the last tile these read clamped, unused data (no branch, so the
     // load counts stay static)
     load_tile(nxt, p, id_next, g, ctx, k0 + kTile, tid);
     id_next = tile_block_id(p, trow, k0 + 2 * kTile, tid);
-    const uint16_t* ks = ks_base + buf * (kTile * kKRow);
-    const uint16_t* vt = vt_base + buf * (kD * kVRow);
+    const uint16_t* ks = ks_buf[buf];
+    const uint16_t* vt = vt_buf[buf];
 
     // S^T = K . Q^T  (scores before scaling)
     f32x16 s[2][2];  // [kt][qt]
@@ -284,8 +268,8 @@ __device__ __forceinline__ void run_key_tiles(QTileState& st, const PParams& p, 
         }
       lsum[qt] = l0 + l1;
     };
-    weights(0, st.m_ref[0]);
-    weights(1, st.m_ref[1]);
+    weights(0, m_ref[0]);
+    weights(1, m_ref[1]);
 
     // Exact-max path, wave-uniform and rare: a weight may exceed the bound
     // (a score rose well above the reference), or a column has no reference
@@ -294,7 +278,7 @@ __device__ __forceinline__ void run_key_tiles(QTileState& st, const PParams& p, 
     // shift identity the result does not depend on the reference used.
     bool redo = false;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) redo = redo || !(lsum[qt] <= kLazyBound) || !st.has_ref[qt];
+    for (int qt = 0; qt < 2; ++qt) redo = redo || !(lsum[qt] <= kLazyBound) || !has_ref[qt];
     if (__builtin_amdgcn_ballot_w64(redo) != 0) {
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
@@ -306,51 +290,45 @@ __device__ __forceinline__ void run_key_tiles(QTileState& st, const PParams& p, 
         const float mx = fmaxf(v, shfl_xor(v, 32)) * c2;  // tile max, log2 units
         // no visible key yet: stay without a reference (weights are 0)
         if (mx != -INFINITY && mx == mx) {
-          const float m_new = st.has_ref[qt] ? fmaxf(st.m_ref[qt], mx) : mx;
-          const float alpha = st.has_ref[qt] ? __builtin_amdgcn_exp2f(st.m_ref[qt] - m_new) : 0.f;
-          st.l_run[qt] *= alpha;
+          const float m_new = has_ref[qt] ? fmaxf(m_ref[qt], mx) : mx;
+          const float alpha = has_ref[qt] ? __builtin_amdgcn_exp2f(m_ref[qt] - m_new) : 0.f;
+          l_run[qt] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) st.o[dt][qt][r] *= alpha;
-          st.m_ref[qt] = m_new;
-          st.has_ref[qt] = true;
+            for (int r = 0; r < 16; ++r) o[dt][qt][r] *= alpha;
+          m_ref[qt] = m_new;
+          has_ref[qt] = true;
         }
-        weights(qt, st.m_ref[qt]);
+        weights(qt, m_ref[qt]);
       }
     }
-    st.l_run[0] += lsum[0];
-    st.l_run[1] += lsum[1];
+    l_run[0] += lsum[0];
+    l_run[1] += lsum[1];
 
     // O^T += V^T . P^T
 #pragma unroll
-    for (int stp = 0; stp < 4; ++stp) {
-      const int kb = stp * 16;  // key offset of this 16-key step within the tile
+    for (int st = 0; st < 4; ++st) {
+      const int kb = st * 16;  // key offset of this 16-key step within the tile
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
         const uint16_t* vrow = vt + (dt * 32 + lr) * kVRow + kb + 4 * lh;
         const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
         const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
         const bf16x8_t a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-        st.o[dt][0] = mfma(a, pop[0][stp], st.o[dt][0]);
-        st.o[dt][1] = mfma(a, pop[1][stp], st.o[dt][1]);
+        o[dt][0] = mfma(a, pop[0][st], o[dt][0]);
+        o[dt][1] = mfma(a, pop[1][st], o[dt][1]);
       }
     }
 
-    store_tile(nxt, ks_base + (buf ^ 1) * (kTile * kKRow), vt_base + (buf ^ 1) * (kD * kVRow),
-               tid);
+    store_tile(nxt, ks_buf[buf ^ 1], vt_buf[buf ^ 1], tid);
     __syncthreads();
   }
-}
 
-// out[row][h][d] = O^T[d][row] / l(row) for the rows of query tile q0 that
-// lie in the prompt; columns without a visible key give zero rows.
-__device__ __forceinline__ void write_rows(const QTileState& st, const PParams& p, int qs,
-                                           int q_len, int q0, int h, int lane) {
-  const int lr = lane & 31, lh = lane >> 5;
+  // epilogue: out[row][h][d] = O^T[d][row] / l(row)
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
-    const float lt = st.l_run[qt] + shfl_xor(st.l_run[qt], 32);
+    const float lt = l_run[qt] + shfl_xor(l_run[qt], 32);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     const int row = q0 + qt * 32 + lr;
     if (row >= q_len) continue;
@@ -360,8 +338,8 @@ __device__ __forceinline__ void write_rows(const QTileState& st, const PParams& 
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int d = dt * 32 + 8 * gq + 4 * lh;
-        const float x0 = st.o[dt][qt][4 * gq + 0] * inv, x1 = st.o[dt][qt][4 * gq + 1] * inv;
-        const float x2 = st.o[dt][qt][4 * gq + 2] * inv, x3 = st.o[dt][qt][4 * gq + 3] * inv;
+        const float x0 = o[dt][qt][4 * gq + 0] * inv, x1 = o[dt][qt][4 * gq + 1] * inv;
+        const float x2 = o[dt][qt][4 * gq + 2] * inv, x3 = o[dt][qt][4 * gq + 3] * inv;
         if (p.out_f32) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + base + d) =
               make_float4(x0, x1, x2, x3);
@@ -371,159 +349,6 @@ __device__ __forceinline__ void write_rows(const QTileState& st, const PParams& 
         }
       }
   }
-}
-
-// Records of halves of split query tiles: each piece has its own 64 KB of
-// O (addressed through a per-record descriptor, so the workspace may exceed
-// 4 GB) and 4 KB of (m, l).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_o(const PParams& p, int record) {
-  return __builtin_amdgcn_make_buffer_rsrc(p.ws_o + (int64_t)record * (kRecOBytes / 4), (short)0,
-                                           kRecOBytes, kRsrcWord3);
-}
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_ml(const PParams& p, int record) {
-  return __builtin_amdgcn_make_buffer_rsrc(p.ws_ml + (int64_t)record * (kRecMLBytes / 4),
-                                           (short)0, kRecMLBytes, kRsrcWord3);
-}
-
-// This wavefront's piece of a split query tile: O unnormalised in register
-// order, (m, l) per column set (m = -inf for columns without a visible key).
-__device__ __forceinline__ void store_record(const QTileState& st, const PParams& p, int record,
-                                             int wave, int lane) {
-  const __amdgpu_buffer_rsrc_t ro = rec_o(p, record);
-  const int obase = wave * (16 * 64 * 16) + lane * 16;
-#pragma unroll
-  for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const f32x4 v = {st.o[dt][qt][4 * j], st.o[dt][qt][4 * j + 1], st.o[dt][qt][4 * j + 2],
-                         st.o[dt][qt][4 * j + 3]};
-        __builtin_amdgcn_raw_buffer_store_b128(v, ro, obase + ((dt * 2 + qt) * 4 + j) * 1024, 0,
-                                               kSc1);
-      }
-  const __amdgpu_buffer_rsrc_t rml = rec_ml(p, record);
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const f32x2 ml = {st.has_ref[qt] ? st.m_ref[qt] : -INFINITY, st.l_run[qt]};
-    __builtin_amdgcn_raw_buffer_store_b64(ml, rml, (wave * 2 + qt) * 512 + lane * 8, 0, kSc1);
-  }
-}
-
-// Fold one stored piece into st: log-sum-exp combination.  Starting from a
-// reset state, folding a piece reproduces it exactly.
-__device__ __forceinline__ void fold_record(QTileState& st, const PParams& p, int record,
-                                            int wave, int lane) {
-  const __amdgpu_buffer_rsrc_t ro = rec_o(p, record);
-  const __amdgpu_buffer_rsrc_t rml = rec_ml(p, record);
-  const int obase = wave * (16 * 64 * 16) + lane * 16;
-  f32x4 ov[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k)
-    ov[k] = __builtin_amdgcn_raw_buffer_load_b128(ro, obase + k * 1024, 0, kSc1);
-  f32x2 ml[2];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
-    ml[qt] = __builtin_amdgcn_raw_buffer_load_b64(rml, (wave * 2 + qt) * 512 + lane * 8, 0, kSc1);
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const float mp = ml[qt][0], lp = ml[qt][1];
-    const float mo = st.has_ref[qt] ? st.m_ref[qt] : -INFINITY;
-    const float mn = fmaxf(mo, mp);
-    const float mu = mn == -INFINITY ? 0.f : mn;
-    const float a = __builtin_amdgcn_exp2f(mo - mu);  // 0 for -inf
-    const float w = __builtin_amdgcn_exp2f(mp - mu);
-    st.l_run[qt] = st.l_run[qt] * a + lp * w;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          st.o[dt][qt][4 * j + e] = st.o[dt][qt][4 * j + e] * a + ov[(dt * 2 + qt) * 4 + j][e] * w;
-    st.m_ref[qt] = mu;
-    st.has_ref[qt] = mn != -INFINITY;
-  }
-}
-
-// Wait until every store this wavefront issued has completed (vmcnt 0).
-__device__ __forceinline__ void drain_stores() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
-// kSplit: query tiles with more than kSplitTiles key tiles are cut in two
-// halves of their key range, each half one workgroup; the half that finishes
-// second folds both records (in key order, so the result does not depend on
-// which half that is), writes the rows and re-zeroes the counter.
-template <bool kSplit>
-__global__ void __launch_bounds__(256, 2)
-prefill_kernel(PParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks_buf[2 * kTile * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_buf[2 * kD * kVRow];
-  __shared__ u32x4 qs_buf[4][2 * 4 * 64];
-  __shared__ uint32_t s_count;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // grid: g fastest, then the half (split form), then b, then query tile from
-  // the last (heaviest) down
-  const int g = blockIdx.x % p.Hkv;
-  int rest = blockIdx.x / p.Hkv;
-  const int half = kSplit ? rest & 1 : 0;
-  if (kSplit) rest >>= 1;
-  const int b = rest % p.B;
-  const int tile = p.tiles_max - 1 - rest / p.B;
-
-  const int qs = p.cu_q_lens[b];
-  const int q_len = p.cu_q_lens[b + 1] - qs;
-  const int q0 = tile * kTile;
-  if (q0 >= q_len) return;
-  int ctx = p.context_lens[b];
-  const int cap = p.max_blocks * kBS;
-  ctx = ctx > cap ? cap : ctx;
-  const int hist = ctx - q_len;  // position of query row 0 minus 0
-  const int rows = q_len - q0 < kTile ? q_len - q0 : kTile;
-  const int pos_first = hist + q0;
-  const int pos_last = hist + q0 + rows - 1;
-  int kend = pos_last + 1 < ctx ? pos_last + 1 : ctx;  // keys [0, kend)
-  if (kend < 0) kend = 0;
-  const int n_tiles = (kend + kTile - 1) / kTile;
-  const bool cut = kSplit && n_tiles > kSplitTiles;
-  if (half > 0 && !cut) return;
-  const int kt_a = cut ? half * (n_tiles / 2) : 0;
-  const int kt_b = cut && half == 0 ? n_tiles / 2 : n_tiles;
-  const int h = 4 * g + wave;
-  const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks;
-
-  u32x4* qsw = qs_buf[wave];
-  load_q_operand(qsw, p, qs, q_len, q0, h, lane);
-  QTileState st;
-  reset_state(st);
-  if (kt_b > kt_a)
-    run_key_tiles(st, p, ks_buf, vt_buf, qsw, trow, g, ctx, pos_first, kt_a, kt_b, tid, lane);
-  if (!cut) {
-    write_rows(st, p, qs, q_len, q0, h, lane);
-    return;
-  }
-  // split query tile: its index among all query tiles of the batch is
-  // qs / 64 + b + tile (distinct per tile, below T_q / 64 + B)
-  const int pair = ((qs / kTile + b + tile) * p.Hkv + g);
-  store_record(st, p, 2 * pair + half, wave, lane);
-  drain_stores();
-  __syncthreads();
-  if (tid == 0)
-    s_count = __hip_atomic_fetch_add(p.ws_count + pair, 1u, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (__builtin_amdgcn_readfirstlane(s_count) == 0) return;  // the other half merges
-  reset_state(st);
-  fold_record(st, p, 2 * pair, wave, lane);
-  fold_record(st, p, 2 * pair + 1, wave, lane);
-  write_rows(st, p, qs, q_len, q0, h, lane);
-  if (tid == 0) __hip_atomic_store(p.ws_count + pair, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -550,18 +375,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   if (p.c_log2 < 1e-30f) p.c_log2 = 1e-30f;
   p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
   const int64_t grid = (int64_t)p.tiles_max * a.B * a.Hkv;
-  if (a.workspace) {
-    const PrefillSplitLayout ly = prefill_split_layout(a.B, a.T_q, a.Hkv);
-    char* ws = static_cast<char*>(a.workspace);
-    p.ws_count = reinterpret_cast<uint32_t*>(ws);
-    p.ws_o = reinterpret_cast<float*>(ws + ly.o_offset);
-    p.ws_ml = reinterpret_cast<float*>(ws + ly.ml_offset);
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)(2 * grid)), dim3(256), 0, stream, p);
-  } else {
-    p.ws_count = nullptr;
-    p.ws_o = p.ws_ml = nullptr;
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream, p);
-  }
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -165,12 +165,12 @@ def test_append_nothing_to_do(lib):
 def prefill_call(lib, **kw):
     a = dict(out=FAKE, out_dtype=pkv.PKV_OUT_F32, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE,
              cu=FAKE, B=2, T=20, Hq=32, Hkv=8, D=64, bs=16, maxb=4, N=8, maxq=10, scale=0.125,
-             ws=None, wsb=0, stream=None)
+             stream=None)
     a.update(kw)
     return lib.paged_attention_prefill_causal(
         a["out"], a["out_dtype"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["cu"], a["B"],
         a["T"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["maxb"], a["N"], a["maxq"], a["scale"],
-        a["ws"], a["wsb"], a["stream"])
+        a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -183,26 +183,9 @@ def prefill_call(lib, **kw):
     (dict(maxq=-1), pkv.PKV_ERR_INVALID_ARG),
     (dict(out_dtype=3), pkv.PKV_ERR_INVALID_ARG),
     (dict(scale=float("nan")), pkv.PKV_ERR_INVALID_ARG),
-    (dict(ws=FAKE, wsb=4096), pkv.PKV_ERR_WORKSPACE),
-    (dict(ws=ctypes.c_void_p(0x1004), wsb=1 << 30), pkv.PKV_ERR_WORKSPACE),
-    # 2^25 query tiles x 64 KV heads x 2 records: beyond int32 record numbers
-    (dict(ws=FAKE, wsb=1 << 62, T=(1 << 31) - 1, Hq=256, Hkv=64, maxq=64),
-     pkv.PKV_ERR_UNSUPPORTED),
 ])
 def test_prefill_rejects(lib, kw, code):
     assert prefill_call(lib, **kw) == code
-
-
-def test_prefill_workspace_size(lib):
-    ws = pkv.paged_attention_prefill_workspace_size
-    counters = (6144 // 64 + 6) * 8                      # query tiles x KV heads
-    head = (counters * 4 + 255) // 256 * 256
-    assert ws(6, 6144, 32, 8, 64, 16) == head + 2 * counters * (65536 + 4096)
-    assert ws(1, 0, 4, 1, 64, 16) == 256 + 2 * (65536 + 4096)
-    assert ws(0, 64, 32, 8, 64, 16) == 0 and ws(2, -1, 32, 8, 64, 16) == 0
-    assert ws(6, 64, 32, 8, 128, 16) == 0 and ws(6, 64, 32, 8, 64, 32) == 0
-    assert ws(6, 64, 16, 8, 64, 16) == 0
-    assert ws(1, (1 << 31) - 1, 256, 64, 64, 16) == 0    # records beyond int32
 
 
 def test_prefill_empty_is_a_noop(lib):

@@ -1,7 +1,7 @@
 """The library's launches captured in a HIP graph replay correctly.
 
 A decode step (kv_append + decode with a split, and the combined
-append + decode call) and a prefill in both launch forms are captured
+append + decode call) and a prefill are captured
 once; the graph is replayed several times with eager work and
 synchronisations in between, and every replay is checked against the eager
 result (bit for bit: same kernels, same inputs)."""
@@ -29,8 +29,6 @@ def test_decode_step_and_prefill_graph_replays():
     tp, lp, cu, qp = dev(p.block_tables), dev(p.context_lens), dev(p.cu_q_lens), dev(p.q)
     pkv.kv_append(kp, vp, dev(p.k_new), dev(p.v_new), tp, lp, cu)
     out_p = torch.empty(tuple(p.q.shape), dtype=torch.float32, device="cuda")
-    out_s = torch.empty_like(out_p)
-    ws_p = pkv.prefill_workspace(p.B, int(p.q.shape[0]), p.Hq, p.Hkv, p.D, 16, "cuda")
     k2, v2 = dev(c.k_cache), dev(c.v_cache)
     out_c = torch.empty_like(out_a)
     ws_c = pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, 16, c.max_context_len, -1, "cuda")
@@ -42,11 +40,10 @@ def test_decode_step_and_prefill_graph_replays():
         pkv.paged_attention_decode(out_f, q, k, v, tables, lens, c.scale, c.max_context_len,
                                    256, ws_f)
         pkv.paged_attention_prefill_causal(out_p, qp, kp, vp, tp, lp, cu, p.scale, 130)
-        pkv.paged_attention_prefill_causal(out_s, qp, kp, vp, tp, lp, cu, p.scale, 130, ws_p)
         pkv.paged_attention_decode_append(out_c, q, k2, v2, kn, vn, tables, lens, c.scale,
                                           c.max_context_len, pkv.PARTITION_AUTO, ws_c)
 
-    outs = (out_a, out_f, out_p, out_s, out_c)
+    outs = (out_a, out_f, out_p, out_c)
     work()
     torch.cuda.synchronize()
     ref = [o.clone() for o in outs]

@@ -1,12 +1,10 @@
 """paged_attention_prefill_causal on the GPU vs the CPU oracle.
 
-Both launch forms are checked on every case: one workgroup per query tile
-(no workspace) and the split form (a workspace; query tiles that see more
-than 16 key tiles are cut into two halves merged by log-sum-exp).  Small problems are compared on every
-output; the full workload (prompts 4 x 512 + 2 x 2048, 32 query / 8 KV heads)
-on sampled rows the oracle computes one by one (first, last and random rows
-of every prompt).  Bar: max-abs <= 1e-2, mean-abs <= 1e-3 for fp32 output;
-bf16 output within max(1e-2, 1 bf16 ulp) of the oracle rounded to bf16.
+Small problems are compared on every output; the full workload (prompts
+4 x 512 + 2 x 2048, 32 query / 8 KV heads) on sampled rows the oracle computes
+one by one (first, last and random rows of every prompt).  Bar: max-abs
+<= 1e-2, mean-abs <= 1e-3 for fp32 output; bf16 output within max(1e-2,
+1 bf16 ulp) of the oracle rounded to bf16.
 """
 import numpy as np
 import pytest
@@ -31,36 +29,17 @@ def appended(p):
     return k, v, kr, vr
 
 
-_WS = {}
-
-
-def split_workspace():
-    """One zero-filled workspace shared by every split call of this module
-    (each call must leave its counters at zero for the next)."""
-    if "ws" not in _WS:
-        _WS["ws"] = pkv.prefill_workspace(16, 8192, 32, 8, 64, 16, "cuda")
-    return _WS["ws"]
-
-
-def gpu_prefill(p, k, v, out_dtype=torch.float32, scale=None, split=False):
+def gpu_prefill(p, k, v, out_dtype=torch.float32, scale=None):
     out = torch.full(tuple(p.q.shape), float("nan"), dtype=out_dtype, device="cuda")
     qlens = (p.cu_q_lens[1:] - p.cu_q_lens[:-1])
     pkv.paged_attention_prefill_causal(out, dev(p.q), k, v, dev(p.block_tables),
                                        dev(p.context_lens), dev(p.cu_q_lens),
                                        p.scale if scale is None else scale,
-                                       int(qlens.max()) if len(qlens) else 0,
-                                       split_workspace() if split else None)
+                                       int(qlens.max()) if len(qlens) else 0)
     torch.cuda.synchronize()
-    if split:
-        assert int(split_workspace()[:65536].view(torch.int32).abs().sum()) == 0, \
-            "split counters not back at zero"
     return out
 
 
-SPLIT = pytest.mark.parametrize("split", [False, True], ids=["per_tile", "split"])
-
-
-@SPLIT
 @pytest.mark.parametrize("prompts,history", [
     ([1, 5, 64, 65, 100, 130], None),
     ([17, 200, 3], [0, 0, 0]),
@@ -68,30 +47,28 @@ SPLIT = pytest.mark.parametrize("split", [False, True], ids=["per_tile", "split"
     ([300], [717]),
     ([0, 40, 0, 1], None),                   # empty prompts in the batch
 ])
-def test_small_full_check(prompts, history, split):
+def test_small_full_check(prompts, history):
     p = wl.prefill_case(prompts=prompts, history=history, num_blocks=256, seed=71, poison=True)
     k, v, kr, vr = appended(p)
     ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
                                 p.cu_q_lens.numpy(), p.scale)
-    got = gpu_prefill(p, k, v, split=split)
-    assert_close(got.cpu().numpy(), ref, f"prefill {prompts} hist {history} split={split}")
-    got16 = gpu_prefill(p, k, v, torch.bfloat16, split=split)
-    assert_close_bf16(got16.cpu(), ref, f"prefill {prompts} split={split}")
+    got = gpu_prefill(p, k, v)
+    assert_close(got.cpu().numpy(), ref, f"prefill {prompts} hist {history}")
+    got16 = gpu_prefill(p, k, v, torch.bfloat16)
+    assert_close_bf16(got16.cpu(), ref, f"prefill {prompts}")
 
 
-@SPLIT
 @pytest.mark.parametrize("scale", [-0.125, 0.0, 0.3])
-def test_scale_sign_and_zero(scale, split):
+def test_scale_sign_and_zero(scale):
     p = wl.prefill_case(prompts=[70, 9], num_blocks=64, seed=72, poison=True)
     k, v, kr, vr = appended(p)
     ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
                                 p.cu_q_lens.numpy(), scale)
-    got = gpu_prefill(p, k, v, scale=scale, split=split)
-    assert_close(got.cpu().numpy(), ref, f"prefill scale {scale} split={split}")
+    got = gpu_prefill(p, k, v, scale=scale)
+    assert_close(got.cpu().numpy(), ref, f"prefill scale {scale}")
 
 
-@SPLIT
-def test_context_shorter_than_prompt(split):
+def test_context_shorter_than_prompt():
     """Rows whose position is negative see no key and give zero rows (a whole
     first query tile of them included)."""
     p = wl.prefill_case(prompts=[150, 40], num_blocks=64, seed=75)
@@ -99,17 +76,16 @@ def test_context_shorter_than_prompt(split):
     k, v = dev(p.k_cache), dev(p.v_cache)
     ref = oracle.prefill_causal(u16(p.q), u16(p.k_cache), u16(p.v_cache), p.block_tables.numpy(),
                                 p.context_lens.numpy(), p.cu_q_lens.numpy(), p.scale)
-    got = gpu_prefill(p, k, v, split=split).cpu()
+    got = gpu_prefill(p, k, v).cpu()
     assert torch.all(got[:120] == 0)
-    assert_close(got.numpy(), ref, f"short context split={split}")
+    assert_close(got.numpy(), ref, "short context")
 
 
-@SPLIT
-def test_row_equals_decode_at_its_position(split):
+def test_row_equals_decode_at_its_position():
     """Prefill row t and a decode whose context ends at t's position agree."""
     p = wl.prefill_case(prompts=[45, 90], history=[20, 0], num_blocks=64, seed=73)
     k, v, _, _ = appended(p)
-    got = gpu_prefill(p, k, v, split=split).cpu()
+    got = gpu_prefill(p, k, v).cpu()
     rows = [0, 7, 44, 45, 80, 134]
     for t in rows:
         b = 0 if t < 45 else 1
@@ -124,12 +100,11 @@ def test_row_equals_decode_at_its_position(split):
         assert err <= 1e-2, (t, err)
 
 
-@SPLIT
-def test_full_workload_sampled_rows(split):
+def test_full_workload_sampled_rows():
     """4 x 512 + 2 x 2048 prompts; every prompt's first, last and random rows."""
     p = wl.prefill_case()
     k, v, kr, vr = appended(p)
-    got = gpu_prefill(p, k, v, split=split).cpu().numpy()
+    got = gpu_prefill(p, k, v).cpu().numpy()
     rng = np.random.default_rng(5)
     rows = []
     for b in range(p.B):
@@ -141,50 +116,9 @@ def test_full_workload_sampled_rows(split):
     assert np.all(np.isfinite(got))
 
 
-@SPLIT
-def test_repeatable_bits(split):
+def test_repeatable_bits():
     p = wl.prefill_case(prompts=[130, 64], num_blocks=64, seed=74)
     k, v, _, _ = appended(p)
-    a = gpu_prefill(p, k, v, split=split)
-    b = gpu_prefill(p, k, v, split=split)
+    a = gpu_prefill(p, k, v)
+    b = gpu_prefill(p, k, v)
     assert torch.equal(a, b)
-
-
-def test_split_matches_per_tile_full_workload():
-    """Every row of the full workload: the two launch forms agree to the
-    decode tolerance (they differ only in where query tiles are cut), and
-    split rows of the longest prompts are checked against the oracle."""
-    p = wl.prefill_case()
-    k, v, kr, vr = appended(p)
-    a = gpu_prefill(p, k, v).cpu().numpy()
-    b = gpu_prefill(p, k, v, split=True).cpu().numpy()
-    err = np.abs(a - b)
-    assert err.max() <= 1e-2 and err.mean() <= 1e-4, (err.max(), err.mean())
-    # rows of the 2048-token prompts around every 64-row query tile boundary
-    rows = []
-    for bseq in (4, 5):
-        s = int(p.cu_q_lens[bseq])
-        rows += [s + 64 * j + o for j in range(0, 32, 5) for o in (0, 63)]
-    ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
-                                p.cu_q_lens.numpy(), p.scale, rows=rows)
-    assert_close(b[rows], ref[rows], "split long prompts")
-
-
-def test_split_workspace_reused_across_shapes():
-    """One workspace, different batches in turn: results match the oracle and
-    the counters are zero after each call (checked in gpu_prefill)."""
-    cases = [wl.prefill_case(prompts=[700, 33], num_blocks=128, seed=76),
-             wl.prefill_case(prompts=[5, 64, 129, 1000], history=[3, 0, 60, 0], num_blocks=256,
-                             seed=77),
-             wl.prefill_case(prompts=[2048], num_blocks=160, seed=78)]
-    for rep in range(2):
-        for p in cases:
-            k, v, kr, vr = appended(p)
-            got = gpu_prefill(p, k, v, split=True).cpu().numpy()
-            qlens = (p.cu_q_lens[1:] - p.cu_q_lens[:-1]).tolist()
-            rows = sorted({int(p.cu_q_lens[b]) + o for b in range(p.B)
-                           for o in (0, qlens[b] // 2, qlens[b] - 1) if qlens[b] > 0})
-            ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(),
-                                        p.context_lens.numpy(), p.cu_q_lens.numpy(), p.scale,
-                                        rows=rows)
-            assert_close(got[rows], ref[rows], f"reuse {qlens} rep {rep}")
