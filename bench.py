@@ -3,23 +3,26 @@
 One step = one decode step of the ragged continuous-batching workload:
 64 sequences (context log-uniform in [16, 8192], block_size 16, 65536-block
 bf16 pool per layer, Llama-3.2-1B attention shapes: 32 query heads, 8 KV
-heads, head_dim 64), and for each of the 16 layers one
-    paged_attention_decode_append
+heads, head_dim 64): one paged_attention_decode_plan (the balanced split's
+plan for this step's lengths and tables, shared by every layer), then for
+each of the 16 layers one
+    paged_attention_decode_append(..., PKV_PARTITION_PLANNED)
 call: store one new token per sequence (kv_append) and attend to the whole
-context (paged_attention_decode) with the automatic balanced split, in one
-kernel launch whose log-sum-exp merge runs inside the kernel.  `--two-calls`
-times kv_append followed by paged_attention_decode per layer instead.  The
-step is captured once in a HIP graph and replayed.
+context (paged_attention_decode) with the balanced split, in one kernel
+launch whose log-sum-exp merge runs inside the kernel.  `--form auto` times
+the same calls without a plan, `--form two-calls` kv_append followed by
+paged_attention_decode per layer.  The step is captured once in a HIP graph
+and replayed.
 
 Prints ONE JSON line.  `value` is the whole step's algorithmic HBM bytes
 divided by the step time (inputs resident in HBM).  `roofline` is for the
 dominant kernel -- the combined append + decode kernel (the decode kernel
-with --two-calls) -- timed with HIP events over graph replays of its 16
+with --form two-calls) -- timed with HIP events over graph replays of its 16
 calls on the stream the graph runs on.  `cpu_baseline` is the CPU oracle on
 a bounded sample of the same workload.  `prefill` reports the causal paged
 prefill workload (4 x 512 + 2 x 2048 prompts) on the bf16 MFMA roofline.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--two-calls]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--form planned|auto|two-calls]
 """
 import argparse
 import hashlib
@@ -45,8 +48,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for counter scaling)")
-    ap.add_argument("--two-calls", action="store_true",
-                    help="kv_append then paged_attention_decode per layer (two launches)")
+    ap.add_argument("--form", choices=("planned", "auto", "two-calls"), default="planned",
+                    help="planned: one plan per step + combined calls; auto: combined calls "
+                         "without a plan; two-calls: kv_append then paged_attention_decode")
     ap.add_argument("--partition", type=int, default=-1,
                     help="decode partition_size (-1 = automatic balanced split)")
     return ap.parse_args()
@@ -72,10 +76,10 @@ def append_bytes(T_new, Hkv, D):
     return T_new * Hkv * D * 2 * 2 * 2  # K and V rows, read + write
 
 
-def traffic_from_profiles(kernel_hash, fused):
-    """HBM bytes per launch of the timed kernel (combined append + decode, or
-    decode alone) from committed counter runs, if they were taken on this
-    exact kernel source; else None."""
+def traffic_from_profiles(kernel_hash, form):
+    """HBM bytes per launch of the timed kernel (combined append + decode with
+    or without a plan, or decode alone) from committed counter runs, if they
+    were taken on this exact kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "decode_ragged_traffic.json")
     try:
         with open(path) as f:
@@ -84,7 +88,9 @@ def traffic_from_profiles(kernel_hash, fused):
         return None
     if rec.get("kernel_source_hash") != kernel_hash:
         return None
-    return rec.get("bytes_per_append_decode_call" if fused else "bytes_per_decode_call")
+    key = {"planned": "bytes_per_planned_append_decode_call",
+           "auto": "bytes_per_append_decode_call", "two-calls": "bytes_per_decode_call"}[form]
+    return rec.get(key)
 
 
 def cpu_baseline(case, k_layers, v_layers, min_seconds=10.0):
@@ -172,6 +178,7 @@ def main():
     max_ctx = case.max_context_len
     outs = [torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(LAYERS)]
     ws = pkv.decode_workspace(B, Hq, Hkv, D, 16, max_ctx, args.partition, dev)
+    ws_plan = pkv.decode_workspace(B, Hq, Hkv, D, 16, max_ctx, pkv.PARTITION_PLANNED, dev)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -180,6 +187,16 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    def planned_calls():
+        for layer in range(LAYERS):
+            pkv.paged_attention_decode_append(outs[layer], q, k_layers[layer], v_layers[layer],
+                                              k_new, v_new, tables, lens, case.scale, max_ctx,
+                                              pkv.PARTITION_PLANNED, ws_plan)
+
+    def planned_step():
+        pkv.paged_attention_decode_plan(k_layers[0], tables, lens, Hq, max_ctx, ws_plan)
+        planned_calls()
 
     def fused_step():
         for layer in range(LAYERS):
@@ -198,9 +215,10 @@ def main():
             pkv.paged_attention_decode(outs[layer], q, k_layers[layer], v_layers[layer], tables,
                                        lens, case.scale, max_ctx, args.partition, ws)
 
-    step, other = (two_call_step, fused_step) if args.two_calls else (fused_step, two_call_step)
+    forms = {"planned": planned_step, "auto": fused_step, "two-calls": two_call_step}
+    step = forms[args.form]
     # Eager warm-up, then capture the step (and, for comparison, the other
-    # form of the step and the decode calls alone) in HIP graphs: host-side
+    # forms of the step and the decode calls alone) in HIP graphs: host-side
     # submission of 16-32 launches would otherwise be slower than the GPU work.
     # Every step stores the same new rows again, so repeated steps see the
     # same pools.
@@ -209,11 +227,13 @@ def main():
     torch.cuda.synchronize()
     eager = [o.clone() for o in outs]
     graphs = {}
-    for name, fn in (("step", step), ("other", other), ("decode", decode_only)):
+    others = [f for f in forms if f != args.form]
+    for name, fn in ([("step", step)] + [(f, forms[f]) for f in others] +
+                     [("decode", decode_only), ("planned calls", planned_calls)]):
         graphs[name] = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graphs[name]):
             fn()
-    for name in ("step", "other"):
+    for name in ["step"] + others:
         graphs[name].replay()
         torch.cuda.synchronize()
         if not all(torch.equal(a, b) for a, b in zip(eager, outs)):
@@ -241,21 +261,26 @@ def main():
         return ev0.elapsed_time(ev1) * 1e3 / (args.steps * calls)
 
     decode_us = event_us(graphs["decode"], LAYERS)
-    other_ms = event_us(graphs["other"], 1) * 1e-3
+    other_ms = {f: round(event_us(graphs[f], 1) * 1e-3, 4) for f in others}
     lens_list = case.context_lens.tolist()
     dec_b = decode_bytes(lens_list, B, Hq, Hkv, D, 2)
     step_b = LAYERS * (dec_b + append_bytes(B, Hkv, D))
     value = step_b / (ms_per_step * 1e-3) / 1e9
-    if args.two_calls:
-        kernel = "decode_auto_kernel<false> (paged_attention_decode, one launch per layer)"
+    if args.form == "two-calls":
+        kernel = "decode_auto_kernel<false,false> (paged_attention_decode, one launch per layer)"
         kernel_us, kernel_b = decode_us, dec_b
-    else:
-        kernel = ("decode_auto_kernel<true> (paged_attention_decode_append, one launch per "
-                  "layer)")
+    elif args.form == "auto":
+        kernel = ("decode_auto_kernel<true,false> (paged_attention_decode_append, one launch "
+                  "per layer)")
         kernel_us, kernel_b = event_us(graphs["step"], LAYERS), dec_b + append_bytes(B, Hkv, D)
+    else:
+        kernel = ("decode_auto_kernel<true,true> (paged_attention_decode_append with the "
+                  "step's plan, one launch per layer)")
+        kernel_us = event_us(graphs["planned calls"], LAYERS)
+        kernel_b = dec_b + append_bytes(B, Hkv, D)
     achieved = kernel_b / (kernel_us * 1e-6) / 1e9
     khash = source_hash("decode.hip")
-    traffic = traffic_from_profiles(khash, not args.two_calls)
+    traffic = traffic_from_profiles(khash, args.form)
 
     result = {
         "metric": "paged decode attention: achieved HBM GB/s (% of peak) and seq-tokens/s",
@@ -273,8 +298,10 @@ def main():
         "config": {"workload": "ragged continuous-batching decode: batch 64, context "
                                "log-uniform [16, 8192], 32q/8kv heads, head_dim 64, "
                                "block_size 16, 65536-block pool per layer, 16 layers per step "
-                               + ("(kv_append + decode each)" if args.two_calls else
-                                  "(one combined append + decode call each)"),
+                               + {"planned": "(one plan per step, one combined append + decode "
+                                             "call per layer)",
+                                  "auto": "(one combined append + decode call per layer)",
+                                  "two-calls": "(kv_append + decode per layer)"}[args.form],
                    "batch": B, "layers": LAYERS, "context_tokens": sum(lens_list),
                    "max_context": max_ctx, "partition_size": args.partition},
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -284,9 +311,7 @@ def main():
                      "traffic": traffic, "kernel": kernel,
                      "us_per_call": round(kernel_us, 2), "algorithmic_bytes": kernel_b,
                      "kernel_source_hash": khash},
-        "other_step_form": {"form": "one combined call per layer" if args.two_calls else
-                            "kv_append + paged_attention_decode per layer",
-                            "ms_per_step": round(other_ms, 4)},
+        "other_step_forms_ms_per_step": other_ms,
         "decode_only_us_per_call": round(decode_us, 2),
     }
 

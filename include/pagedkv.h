@@ -72,6 +72,7 @@ extern "C" {
 /* partition_size values for paged_attention_decode besides a positive size */
 #define PKV_PARTITION_NONE 0  /* one wavefront per (sequence, KV head)        */
 #define PKV_PARTITION_AUTO (-1) /* balanced split of all blocks over the GPU  */
+#define PKV_PARTITION_PLANNED (-2) /* PKV_PARTITION_AUTO from a stored plan      */
 
 /* Text describing the last non-OK status returned on the calling thread. */
 PKV_API const char *pagedkv_last_error(void);
@@ -129,6 +130,11 @@ PKV_API size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int3
  *               PKV_PARTITION_AUTO: all blocks of the batch are cut into equal
  *               shares, one per wavefront of a fixed grid, and streams cut
  *               across shares are merged the same way.
+ *               PKV_PARTITION_PLANNED: the same split, read from a plan that
+ *               paged_attention_decode_plan stored in this workspace (see
+ *               there); a plan made for other B, Hkv, max_blocks_per_seq,
+ *               num_blocks or max_context_len is ignored and the split is
+ *               computed as for PKV_PARTITION_AUTO.
  * workspace     device scratch of at least
  *               paged_attention_decode_workspace_size(...) bytes (may be NULL
  *               when that is 0).  It must be zero-filled before its first use;
@@ -151,6 +157,35 @@ PKV_API int paged_attention_decode(void *out, int32_t out_dtype, const void *q,
                            int32_t num_blocks, int32_t max_context_len, float scale,
                            int32_t partition_size, void *workspace,
                            size_t workspace_bytes, void *stream);
+
+/* paged_attention_decode_plan -- store the plan of the automatic split for
+ * these lengths and tables in the workspace, for later calls of
+ * paged_attention_decode / _decode_append with PKV_PARTITION_PLANNED.
+ *
+ * Defined by: the calls it serves (the split is a scheduling of the same
+ * attention; guide ch. 6: every layer of a decode step reads the same block
+ * tables and lengths).
+ *
+ * The plan is what the automatic split computes before its first key load:
+ * the prefix of per-sequence block counts, and for each wavefront of its
+ * fixed grid the stream it starts in and the block ids of its first 64 list
+ * positions.  Every layer of a decode step shares block_tables and
+ * context_lens, so one plan per step serves all of them and each call starts
+ * loading keys at once.  A plan describes the contents of block_tables and
+ * context_lens at the time of this call: after they change (the next step),
+ * plan again; a call with a plan whose contents are stale gives wrong
+ * results (it stays inside the pools and the workspace).
+ * Arguments as for paged_attention_decode; the workspace must hold
+ * paged_attention_decode_workspace_size(..., PKV_PARTITION_PLANNED) bytes and
+ * be the one the planned calls pass.  Calls sharing a workspace must not run
+ * concurrently.
+ */
+PKV_API int paged_attention_decode_plan(const int32_t *block_tables,
+                                const int32_t *context_lens, int32_t B, int32_t Hq,
+                                int32_t Hkv, int32_t D, int32_t block_size,
+                                int32_t max_blocks_per_seq, int32_t num_blocks,
+                                int32_t max_context_len, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* paged_attention_decode_append -- one decode step of a layer: store one new
  * token per sequence in the pools (kv_append with cu_new_lens = NULL), then

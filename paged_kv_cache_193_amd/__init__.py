@@ -16,6 +16,8 @@ Entry points (same names as the C ABI in include/pagedkv.h):
               partition_size=AUTO, workspace=None)
     paged_attention_prefill_causal(out, q, k_cache, v_cache, block_tables,
               context_lens, cu_q_lens, scale, max_q_len)
+    paged_attention_decode_plan(k_cache, block_tables, context_lens, Hq,
+              max_context_len, workspace)
     paged_attention_decode_workspace_size(...)
 """
 import ctypes
@@ -32,10 +34,12 @@ PKV_OUT_BF16 = 0
 PKV_OUT_F32 = 1
 PARTITION_NONE = 0
 PARTITION_AUTO = -1
+PARTITION_PLANNED = -2
 
 # every symbol include/pagedkv.h declares
 ABI_SYMBOLS = ("pagedkv_last_error", "kv_append", "paged_attention_decode_workspace_size",
                "paged_attention_decode", "paged_attention_decode_append",
+               "paged_attention_decode_plan",
                "paged_attention_prefill_causal")
 
 _lib = None
@@ -69,6 +73,8 @@ def load_library():
     lib.paged_attention_decode_append.argtypes = [P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                   I, F, I, P, Z, P]
     lib.paged_attention_decode_append.restype = ctypes.c_int
+    lib.paged_attention_decode_plan.argtypes = [P, P, I, I, I, I, I, I, I, I, P, Z, P]
+    lib.paged_attention_decode_plan.restype = ctypes.c_int
     lib.paged_attention_prefill_causal.argtypes = [P, I, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                    I, I, F, P]
     lib.paged_attention_prefill_causal.restype = ctypes.c_int
@@ -193,6 +199,21 @@ def paged_attention_decode_append(out, q, k_cache, v_cache, k_new, v_new, block_
         _dev(block_tables, torch.int32, "block_tables"),
         _dev(context_lens, torch.int32, "context_lens"), B, Hq, Hkv, D, bs, maxb, N,
         int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes, _stream()))
+
+
+def paged_attention_decode_plan(k_cache, block_tables, context_lens, Hq, max_context_len,
+                                workspace):
+    """Store the automatic split's plan for these tables and lengths in
+    `workspace` (sized for PARTITION_PLANNED), for decode calls with
+    partition_size=PARTITION_PLANNED.  k_cache only supplies the pool shape."""
+    torch = _torch()
+    N, Hkv, bs, D = k_cache.shape
+    B, maxb = block_tables.shape
+    _check(load_library().paged_attention_decode_plan(
+        _dev(block_tables, torch.int32, "block_tables"),
+        _dev(context_lens, torch.int32, "context_lens"), B, Hq, Hkv, D, bs, maxb, N,
+        int(max_context_len), _dev(workspace, torch.uint8, "workspace"), workspace.numel(),
+        _stream()))
 
 
 def paged_attention_prefill_causal(out, q, k_cache, v_cache, block_tables, context_lens,

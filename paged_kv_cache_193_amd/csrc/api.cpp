@@ -36,7 +36,8 @@ constexpr int kD = 64, kBS = 16, kGroup = 4;
 // Decode mode and split geometry for the given arguments.
 struct DecodePlan {
   int mode, part_blocks, parts_max;
-  size_t records, bytes;
+  bool planned;        // PKV_PARTITION_PLANNED: the plan region follows the records
+  size_t records, bytes, plan_offset;
 };
 
 int plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
@@ -54,7 +55,9 @@ int plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_siz
   plan->mode = pkv::kWhole;
   plan->part_blocks = 0;
   plan->parts_max = 1;
-  if (partition_size == PKV_PARTITION_AUTO) {
+  plan->planned = partition_size == PKV_PARTITION_PLANNED;
+  plan->plan_offset = 0;
+  if (partition_size == PKV_PARTITION_AUTO || plan->planned) {
     if (B > pkv::kAutoMaxBatch)
       return fail(PKV_ERR_UNSUPPORTED, "automatic split handles B <= %d (got %d)",
                   pkv::kAutoMaxBatch, B);
@@ -87,6 +90,10 @@ int plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_siz
                   plan->records, pkv::kMaxRecords);
     // counter region, then records (normalised outputs) and their (m, l) pairs
     plan->bytes = pkv::kCounterBytes + plan->records * (pkv::kRecordFloats + 8) * sizeof(float);
+  }
+  if (plan->planned) {
+    plan->plan_offset = (plan->bytes + 255) / 256 * 256;
+    plan->bytes = plan->plan_offset + pkv::kPlanBytes;
   }
   return PKV_OK;
 }
@@ -191,6 +198,10 @@ int prepare_decode(void* out, int32_t out_dtype, const void* q, const void* k_ca
   a->ws_ml = plan.bytes ? rec + plan.records * pkv::kRecordFloats : nullptr;
   a->k_new = nullptr;
   a->v_new = nullptr;
+  a->plan = plan.planned ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) +
+                                                       plan.plan_offset)
+                         : nullptr;
+  a->write_plan = 0;
   return PKV_OK;
 }
 
@@ -247,6 +258,39 @@ int paged_attention_decode_append(void* out, int32_t out_dtype, const void* q, v
   if (rc2 != PKV_OK) return rc2;
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream),
                     "paged_attention_decode_append launch (decode)");
+}
+
+int paged_attention_decode_plan(const int32_t* block_tables, const int32_t* context_lens,
+                                int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                int32_t block_size, int32_t max_blocks_per_seq,
+                                int32_t num_blocks, int32_t max_context_len, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  DecodePlan plan;
+  const int rc = plan_decode(B, Hq, Hkv, D, block_size, max_context_len, PKV_PARTITION_PLANNED,
+                             &plan);
+  if (rc != PKV_OK) return rc;
+  if (B == 0) return PKV_OK;
+  if (!block_tables || !context_lens) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (max_blocks_per_seq <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq and num_blocks must be > 0");
+  if (!workspace || workspace_bytes < plan.bytes)
+    return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned16(workspace)) return fail(PKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  pkv::DecodeArgs a{};
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_context_len = max_context_len;
+  a.mode = pkv::kAuto;
+  a.parts_max = 1;
+  a.plan = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + plan.plan_offset);
+  a.write_plan = 1;
+  return hip_status(pkv::launch_decode(a, (hipStream_t)stream), "paged_attention_decode_plan launch");
 }
 
 int paged_attention_prefill_causal(void* out, int32_t out_dtype, const void* q,

@@ -85,6 +85,7 @@ struct Params {
   int n_records;       // records in ws_o / ws_ml
   const uint16_t* k_new;  // append variant: the new token's K / V rows [B][Hkv][D]
   const uint16_t* v_new;
+  int32_t* plan;          // planned variant: the plan region of the workspace
 };
 
 // Split records are written and read with 16-byte buffer accesses at agent
@@ -670,7 +671,7 @@ __device__ __forceinline__ void cursor_advance(Cursor& c, const int* s_ctx, int 
   c.g = 0;
   int b = c.b + 1;
   while (b < B - 1 && __builtin_amdgcn_readfirstlane(s_ctx[b]) == 0) ++b;
-  cursor_load_seq(c, s_ctx, b);
+  cursor_load_seq(c, s_ctx, b < B ? b : B - 1);  // b < B whenever a group follows
 }
 
 // Block-id window: lane k returns the physical id of block xs + k of the
@@ -690,10 +691,12 @@ __device__ __forceinline__ int id_window(const Params& p, const int* s_ctx, cons
       do {
         ++b;
       } while (b < p.B - 1 && s_ctx[b] == 0);
+      if (b >= p.B) return -1;  // not reached while the list holds xs + lane
       nbr = (s_ctx[b] + kBS - 1) / kBS;
       nbp = (nbr + kRing - 1) / kRing * kRing;
     }
   }
+  if (nbr <= 0) return -1;  // not reached: streams without blocks are not in the list
   j += k;
   const int jj = j < nbr - 1 ? j : nbr - 1;
   return p.block_tables[(int64_t)b * p.max_blocks + jj];
@@ -727,27 +730,27 @@ __device__ __forceinline__ void reset_state(LaneState& st) {
     for (int e = 0; e < 8; ++e) st.acc[j][e] = 0.f;
 }
 
-//
-// kAppend: the call also stores one new token per sequence (kv_append with
-// one token each).  The new token is the last of its sequence, so it lies in
-// the stream's last block, which exactly one wavefront consumes: that
-// wavefront writes the token's K and V rows into the pools and uses them
-// from registers in place of the (stale) rows its load returned.  The rows
-// of a sequence clamped to max_context_len are stored by a workgroup during
-// set-up; slots outside the table or pool are not written (as kv_append).
-template <bool kAppend>
-__global__ void __launch_bounds__(kWaves * 64)
-decode_auto_kernel(Params p) {
-  __shared__ float red[kWaves][8 * 4 * kD];
-  __shared__ int pfx[kAutoMaxBatch + 1];
-  __shared__ int s_ctx[kAutoMaxBatch];
-  __shared__ int wsum[kWaves];
-  __shared__ unsigned char s_newok[kAppend ? kAutoMaxBatch : 1];  // append this sequence
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// Stream and block of list position x0: largest b with Hkv * pfx[b] <= x0.
+__device__ __forceinline__ void locate_share(Cursor& cc, const Params& p, const int* pfx,
+                                             const int* s_ctx, int64_t x0) {
+  int lo = 0, hi = p.B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)p.Hkv * pfx[mid] <= x0) lo = mid; else hi = mid;
+  }
+  cursor_load_seq(cc, s_ctx, __builtin_amdgcn_readfirstlane(lo));
+  const int64_t off = x0 - (int64_t)p.Hkv * __builtin_amdgcn_readfirstlane(pfx[cc.b]);
+  cc.g = (int)(off / cc.nbp);
+  cc.j = (int)(off - (int64_t)cc.g * cc.nbp);
+}
 
-  // per-sequence padded block counts -> exclusive prefix in LDS
+// Context lengths (clamped) of all sequences and the exclusive prefix of
+// their padded block counts, in LDS (pfx[B] = total); with kAppend also
+// whether each sequence's new token is stored by the wavefronts.
+template <bool kAppend>
+__device__ __forceinline__ void block_prefix(const Params& p, int* pfx, int* s_ctx,
+                                             unsigned char* s_newok, int* wsum, int tid,
+                                             int lane, int wave) {
   const int per = (p.B + kWaves * 64 - 1) / (kWaves * 64);
   const int beg = tid * per;
   const int end = beg + per < p.B ? beg + per : p.B;
@@ -774,6 +777,170 @@ decode_auto_kernel(Params p) {
   }
   if (tid == kWaves * 64 - 1) pfx[p.B] = run;
   __syncthreads();
+}
+
+// The plan of the balanced split for this call's lengths and tables: what
+// decode_auto_kernel computes before its first load (the prefix of padded
+// block counts, each wavefront's first stream and the block ids of its first
+// 64 list positions), stored once so that calls which share lengths and
+// tables (every layer of a decode step) start loading keys at once.
+__global__ void __launch_bounds__(kWaves * 64)
+decode_plan_kernel(Params p) {
+  __shared__ int pfx[kAutoMaxBatch + 1];
+  __shared__ int s_ctx[kAutoMaxBatch];
+  __shared__ int wsum[kWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  block_prefix<false>(p, pfx, s_ctx, nullptr, wsum, tid, lane, wave);
+  const int64_t NB = (int64_t)p.Hkv * __builtin_amdgcn_readfirstlane(pfx[p.B]);
+  const int W = gridDim.x * kWaves;
+  const int64_t G = NB / kRing;
+  const int64_t gbase = G / W;
+  const int64_t rem = G - gbase * W;
+  if (blockIdx.x == 0) {
+    for (int k = tid; k <= p.B; k += kWaves * 64) {
+      p.plan[kPlanHeaderInts + k] = pfx[k];
+      if (k < p.B) p.plan[kPlanCtxOffset + k] = s_ctx[k];
+    }
+    if (tid < kPlanHeaderInts) {
+      const int hdr[7] = {kPlanMagic, p.B, p.Hkv, p.max_blocks, p.ctx_cap, p.num_blocks, W};
+      p.plan[tid] = tid < 7 ? hdr[tid] : 0;
+    }
+  }
+  const int w = blockIdx.x * kWaves + wave;
+  const int64_t x0 = share_start(w, gbase, rem);
+  const int64_t x1 = share_start(w + 1, gbase, rem);
+  int* ent = p.plan + kPlanWaveOffset + (int64_t)w * kPlanWaveInts;
+  Cursor cc = {};
+  int tab = 0;
+  if (x0 < x1) {
+    locate_share(cc, p, pfx, s_ctx, x0);
+    tab = id_window(p, s_ctx, cc, x0, x1, lane);
+  }
+  ent[4 + lane] = tab;
+  if (lane < 4) ent[lane] = lane == 0 ? cc.b : lane == 1 ? cc.g : lane == 2 ? cc.j : cc.ctx;
+}
+
+//
+// kAppend: the call also stores one new token per sequence (kv_append with
+// one token each).  The new token is the last of its sequence, so it lies in
+// the stream's last block, which exactly one wavefront consumes: that
+// wavefront writes the token's K and V rows into the pools and uses them
+// from registers in place of the (stale) rows its load returned.  The rows
+// of a sequence clamped to max_context_len are stored by a workgroup during
+// set-up; slots outside the table or pool are not written (as kv_append).
+template <bool kAppend, bool kPlanned>
+__global__ void __launch_bounds__(kWaves * 64)
+decode_auto_kernel(Params p) {
+  __shared__ float red[kWaves][8 * 4 * kD];
+  __shared__ int pfx[kAutoMaxBatch + 1];
+  __shared__ int s_ctx[kAutoMaxBatch];
+  __shared__ int wsum[kWaves];
+  __shared__ unsigned char s_newok[kAppend ? kAutoMaxBatch : 1];  // append this sequence
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // per-sequence context lengths and the exclusive prefix of their padded
+  // block counts in LDS: read from the plan when one matches this call
+  const int grp = lane >> 3, i = lane & 7;
+  const bool quad1 = (i & 4) != 0;
+  const int c = quad1 ? ((i & 3) ^ 3) : (i & 3);
+  const int own_tok = quad1 ? grp + 8 : grp;
+  const int lane_off = grp * kD + 8 * i;
+  BlockRegs ring[kRing];
+  int nvalid[kRing];
+  bool slast[kRing];  // append: the slot holds its stream's last block
+  int sphys[kRing];   // append: that block's physical id
+  uint32_t qv[4][4], qn[4][4];
+  u32x4 knv, vnv, knn, vnn;  // append: new-token chunks (consumed / next group)
+  // Issue the first group of the share starting at stream position ci
+  // (id window tab, whose lane 0 is the group's first block).
+  auto prologue = [&](const Cursor& ci, int tab) {
+    load_q(qn, p, ci.b, ci.g, i, c);
+    if (kAppend) load_new(knn, vnn, p, ci.b, ci.g, i);
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+      const int j = ci.j + s < ci.nbr - 1 ? ci.j + s : ci.nbr - 1;
+      const int id = __builtin_amdgcn_readlane(tab, s);
+      const int nv = issue_block(ring[s], p, id, ci.g, j, ci.ctx, lane_off);
+      nvalid[s] = ci.j + s < ci.nbr ? nv : 0;
+      if (kAppend) {
+        slast[s] = ci.j + s == ci.nbr - 1 && nv > 0;
+        sphys[s] = id;
+      }
+    }
+  };
+
+  // With a plan: its first group is issued at once, before the plan is
+  // checked against this call (the block ids are range-checked, so the loads
+  // stay inside the pools whatever the plan holds); the context lengths and
+  // the prefix come from the plan too.  A plan made for other lengths or
+  // another shape is not used: the split is computed and the first group
+  // issued again.
+  bool use_plan = false, issued = false;
+  int pl_b = 0, pl_g = 0, pl_j = 0, pl_tab = 0;
+  // this thread's first sequence (k = tid): plan prefix, plan length and
+  // length, loaded before the first group so that waiting for them does not
+  // wait for its keys (vector loads complete in order)
+  int v_pfx = 0, v_pctx = 0, v_len = 0;
+  if (kPlanned) {
+    if (tid <= p.B) v_pfx = p.plan[kPlanHeaderInts + tid];
+    if (tid < p.B) {
+      v_pctx = p.plan[kPlanCtxOffset + tid];
+      v_len = p.context_lens[tid];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int w = blockIdx.x * kWaves + wave;
+    const int* ent = p.plan + kPlanWaveOffset + (int64_t)w * kPlanWaveInts;
+    pl_tab = ent[4 + lane];
+    pl_b = ld_uniform(ent, 0);
+    pl_g = ld_uniform(ent, 1);
+    pl_j = ld_uniform(ent, 2);
+    const int pl_ctx = ld_uniform(ent, 3);
+    use_plan = ld_uniform(p.plan, 0) == kPlanMagic && ld_uniform(p.plan, 1) == p.B &&
+               ld_uniform(p.plan, 2) == p.Hkv && ld_uniform(p.plan, 3) == p.max_blocks &&
+               ld_uniform(p.plan, 4) == p.ctx_cap && ld_uniform(p.plan, 5) == p.num_blocks &&
+               ld_uniform(p.plan, 6) == (int)(gridDim.x * kWaves);
+    if (use_plan && pl_ctx > 0 && pl_ctx <= p.ctx_cap && pl_b >= 0 && pl_b < p.B && pl_g >= 0 &&
+        pl_g < p.Hkv && pl_j >= 0) {
+      Cursor sc;
+      sc.b = pl_b;
+      sc.ctx = pl_ctx;
+      sc.nbr = (pl_ctx + kBS - 1) / kBS;
+      sc.nbp = (sc.nbr + kRing - 1) / kRing * kRing;
+      sc.g = pl_g;
+      sc.j = pl_j;
+      prologue(sc, pl_tab);
+      issued = true;
+    }
+  }
+  if (use_plan) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid == 0) wsum[0] = 0;
+    bool stale = false;
+    for (int k = tid; k <= p.B; k += kWaves * 64) {
+      const bool first = k == tid;
+      pfx[k] = first ? v_pfx : p.plan[kPlanHeaderInts + k];
+      if (k < p.B) {
+        int cx = first ? v_len : p.context_lens[k];
+        if (kAppend) s_newok[k] = cx >= 1 && cx <= p.ctx_cap;
+        cx = cx < 0 ? 0 : (cx > p.ctx_cap ? p.ctx_cap : cx);  // as eff_ctx
+        s_ctx[k] = cx;
+        // the plan must have been made for exactly these lengths
+        stale = stale || (first ? v_pctx : p.plan[kPlanCtxOffset + k]) != cx;
+      }
+    }
+    __syncthreads();
+    if (stale) wsum[0] = 1;
+    __syncthreads();
+    if (wsum[0] != 0) {
+      use_plan = false;
+      __syncthreads();  // everyone has read the flag before wsum is reused
+    }
+  }
+  if (!use_plan) block_prefix<kAppend>(p, pfx, s_ctx, s_newok, wsum, tid, lane, wave);
 
   // ring groups are dealt out as evenly as possible: the first `rem`
   // wavefronts take gbase + 1 groups, the others gbase
@@ -817,50 +984,22 @@ decode_auto_kernel(Params p) {
   const int64_t x1 = share_start(w + 1, gbase, rem);
   if (x0 >= x1) return;
 
-  const int grp = lane >> 3, i = lane & 7;
-  const bool quad1 = (i & 4) != 0;
-  const int c = quad1 ? ((i & 3) ^ 3) : (i & 3);
-  const int own_tok = quad1 ? grp + 8 : grp;
-  const int lane_off = grp * kD + 8 * i;
-
-  // locate x0: largest b with Hkv * pfx[b] <= x0
-  int lo = 0, hi = p.B;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if ((int64_t)p.Hkv * pfx[mid] <= x0) lo = mid; else hi = mid;
-  }
+  // locate x0 (or take it from the plan)
   Cursor cc;
-  cursor_load_seq(cc, s_ctx, __builtin_amdgcn_readfirstlane(lo));
-  {
-    const int64_t off = x0 - (int64_t)p.Hkv * __builtin_amdgcn_readfirstlane(pfx[cc.b]);
-    cc.g = (int)(off / cc.nbp);
-    cc.j = (int)(off - (int64_t)cc.g * cc.nbp);
+  if (use_plan) {
+    cursor_load_seq(cc, s_ctx, pl_b);
+    cc.g = pl_g;
+    cc.j = pl_j;
+  } else {
+    locate_share(cc, p, pfx, s_ctx, x0);
   }
 
   // prologue: id window and q of the first group, then issue it
   Cursor ci = cc;
   int64_t xi = x0;
   int64_t win = x0;
-  int tab = id_window(p, s_ctx, ci, x0, x1, lane);
-  BlockRegs ring[kRing];
-  int nvalid[kRing];
-  bool slast[kRing];  // append: the slot holds its stream's last block
-  int sphys[kRing];   // append: that block's physical id
-  uint32_t qv[4][4], qn[4][4];
-  u32x4 knv, vnv, knn, vnn;  // append: new-token chunks (consumed / next group)
-  load_q(qn, p, ci.b, ci.g, i, c);
-  if (kAppend) load_new(knn, vnn, p, ci.b, ci.g, i);
-#pragma unroll
-  for (int s = 0; s < kRing; ++s) {
-    const int j = ci.j + s < ci.nbr - 1 ? ci.j + s : ci.nbr - 1;
-    const int id = __builtin_amdgcn_readlane(tab, (int)(xi - win) + s);
-    const int nv = issue_block(ring[s], p, id, ci.g, j, ci.ctx, lane_off);
-    nvalid[s] = ci.j + s < ci.nbr ? nv : 0;
-    if (kAppend) {
-      slast[s] = ci.j + s == ci.nbr - 1 && nv > 0;
-      sphys[s] = id;
-    }
-  }
+  int tab = use_plan ? pl_tab : id_window(p, s_ctx, ci, x0, x1, lane);
+  if (!(use_plan && issued)) prologue(ci, tab);
   if (xi + kRing < x1) {
     xi += kRing;
     cursor_advance(ci, s_ctx, p.Hkv, p.B);
@@ -1056,6 +1195,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.n_records = (int)decode_records(a.mode, a.B, a.Hkv, a.parts_max);
   p.k_new = (const uint16_t*)a.k_new;
   p.v_new = (const uint16_t*)a.v_new;
+  p.plan = a.plan;
   const int streams = a.B * a.Hkv;
   if (a.mode == kWhole) {
     const int grid = (streams + kWaves - 1) / kWaves;
@@ -1065,12 +1205,17 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     const int grid = (int)((units + kWaves - 1) / kWaves);
     hipLaunchKernelGGL(decode_units_kernel<kFixed>, dim3(grid), dim3(kWaves * 64), 0, stream, p);
   } else {
-    if (a.k_new)
-      hipLaunchKernelGGL(decode_auto_kernel<true>, dim3(kAutoWaves / kWaves), dim3(kWaves * 64),
-                         0, stream, p);
+    const dim3 grid(kAutoWaves / kWaves), block(kWaves * 64);
+    if (a.write_plan)
+      hipLaunchKernelGGL(decode_plan_kernel, grid, block, 0, stream, p);
+    else if (a.k_new && a.plan)
+      hipLaunchKernelGGL((decode_auto_kernel<true, true>), grid, block, 0, stream, p);
+    else if (a.k_new)
+      hipLaunchKernelGGL((decode_auto_kernel<true, false>), grid, block, 0, stream, p);
+    else if (a.plan)
+      hipLaunchKernelGGL((decode_auto_kernel<false, true>), grid, block, 0, stream, p);
     else
-      hipLaunchKernelGGL(decode_auto_kernel<false>, dim3(kAutoWaves / kWaves), dim3(kWaves * 64),
-                         0, stream, p);
+      hipLaunchKernelGGL((decode_auto_kernel<false, false>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }

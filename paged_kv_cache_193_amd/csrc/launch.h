@@ -43,6 +43,19 @@ constexpr int kMaxSplitStreams = 32768;
 constexpr int kMaxRecords = (1 << 21) - 1;
 constexpr size_t kCounterBytes = (size_t)kMaxSplitStreams * 4;
 
+// Decode plan (partition PKV_PARTITION_PLANNED), after the split records of
+// the balanced split: a header, the per-sequence prefix of padded block
+// counts, the (clamped) context lengths it was made for, and per wavefront
+// its first stream (b, g, j), that stream's length (0: no share) and the
+// block ids of its first 64 list positions.  Written by
+// paged_attention_decode_plan.
+constexpr int kPlanHeaderInts = 16;
+constexpr int kPlanCtxOffset = kPlanHeaderInts + kAutoMaxBatch + 1;
+constexpr int kPlanWaveOffset = kPlanCtxOffset + kAutoMaxBatch;
+constexpr int kPlanWaveInts = 4 + 64;
+constexpr int kPlanMagic = 0x504c414e;
+constexpr size_t kPlanBytes = ((size_t)kPlanWaveOffset + (size_t)kAutoWaves * kPlanWaveInts) * 4;
+
 struct DecodeArgs {
   void* out;
   int32_t out_f32;
@@ -63,6 +76,10 @@ struct DecodeArgs {
   // into the pools before attending (both null: plain decode)
   const void* k_new;
   const void* v_new;
+  // kAuto only: the plan region of the workspace (null: none); with
+  // write_plan the launch computes the plan instead of attending
+  int32_t* plan;
+  int32_t write_plan;
 };
 size_t decode_records(int32_t mode, int32_t B, int32_t Hkv, int32_t parts_max);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

@@ -136,6 +136,40 @@ def test_decode_append_empty_batch_is_a_noop(lib):
                               bt=None, cl=None) == pkv.PKV_OK
 
 
+def plan_call(lib, **kw):
+    a = dict(bt=FAKE, cl=FAKE, B=2, Hq=32, Hkv=8, D=64, bs=16, maxb=4, N=8, maxctx=64, ws=None,
+             wsb=0, stream=None)
+    a.update(kw)
+    return lib.paged_attention_decode_plan(a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                           a["bs"], a["maxb"], a["N"], a["maxctx"], a["ws"],
+                                           a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(D=128), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(B=5000), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(bt=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(maxb=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(ws=None), pkv.PKV_ERR_WORKSPACE),
+    (dict(ws=FAKE, wsb=1 << 20), pkv.PKV_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x1008), wsb=1 << 30), pkv.PKV_ERR_WORKSPACE),
+])
+def test_decode_plan_rejects(lib, kw, code):
+    assert plan_call(lib, **kw) == code
+    assert pkv.last_error()
+
+
+def test_planned_workspace_holds_the_plan(lib):
+    ws = pkv.paged_attention_decode_workspace_size
+    auto = ws(64, 32, 8, 64, 16, 8192, pkv.PARTITION_AUTO)
+    planned = ws(64, 32, 8, 64, 16, 8192, pkv.PARTITION_PLANNED)
+    plan_ints = 16 + 4097 + 4096 + 2048 * 68
+    assert planned == (auto + 255) // 256 * 256 + plan_ints * 4
+    assert decode_call(lib, part=pkv.PARTITION_PLANNED) == pkv.PKV_ERR_WORKSPACE
+    assert plan_call(lib, B=0, bt=None, cl=None) == pkv.PKV_OK
+
+
 def append_call(lib, **kw):
     a = dict(k=FAKE, v=FAKE, kn=FAKE, vn=FAKE, bt=FAKE, cl=FAKE, cu=None, B=2, T=2, Hkv=8, D=64,
              bs=16, maxb=4, N=8, stream=None)
