@@ -46,9 +46,13 @@ class Oracle:
         lib.oracle_decode_partials.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I,
                                                I, I, I, Dbl, I, I]
         lib.oracle_lse_merge.argtypes = [P, P, P, P, I, I, I]
+        lib.oracle_token_positions.argtypes = [P, P, P, P, I, I]
+        lib.oracle_rope.argtypes = [P, P, P, P, P, I, I, I, I]
+        lib.oracle_round_bf16.argtypes = [P, P, ctypes.c_long]
         for f in (lib.oracle_kv_append, lib.oracle_decode, lib.oracle_decode_online,
                   lib.oracle_prefill_causal, lib.oracle_decode_partials,
-                  lib.oracle_lse_merge):
+                  lib.oracle_lse_merge, lib.oracle_token_positions, lib.oracle_rope,
+                  lib.oracle_round_bf16):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -127,6 +131,70 @@ class Oracle:
         _check(rc, "lse_merge")
         return out.reshape(*lead, D)
 
+    def token_positions(self, context_lens, cu_new_lens, T_new):
+        """(pos, seq) int32 [T_new]: absolute position and sequence of every new token."""
+        cl = _i32(context_lens)
+        cu = None if cu_new_lens is None else _i32(cu_new_lens)
+        pos = np.full(T_new, -1, dtype=np.int32)
+        seq = np.full(T_new, -1, dtype=np.int32)
+        rc = self.lib.oracle_token_positions(_ptr(pos), _ptr(seq), _ptr(cl), _ptr(cu),
+                                             cl.shape[0], T_new)
+        _check(rc, "token_positions")
+        return pos, seq
+
+    def rope(self, x, pos, rope_cos, rope_sin):
+        """x [rows][heads][D] uint16 at positions pos [rows] -> float64 [rows][heads][D]."""
+        x = _u16(x)
+        rows, heads, D = x.shape
+        p = _i32(pos)
+        c = np.ascontiguousarray(rope_cos, dtype=np.float32)
+        s = np.ascontiguousarray(rope_sin, dtype=np.float32)
+        assert c.shape == s.shape and c.shape[1] * 2 == D and p.shape == (rows,)
+        out = np.zeros((rows, heads, D), dtype=np.float64)
+        rc = self.lib.oracle_rope(_ptr(out), _ptr(x), _ptr(p), _ptr(c), _ptr(s), rows, heads,
+                                  D, c.shape[0])
+        _check(rc, "rope")
+        return out
+
+    def round_bf16(self, x):
+        """float64 array -> uint16 bf16 bit patterns (nearest, ties to even)."""
+        xd = np.ascontiguousarray(x, dtype=np.float64)
+        out = np.zeros(xd.shape, dtype=np.uint16)
+        self.lib.oracle_round_bf16(_ptr(out), _ptr(xd), xd.size)
+        return out
+
+    def kv_append_rope(self, k_cache, v_cache, k_new, v_new, block_tables, context_lens,
+                       rope_cos, rope_sin, q=None, cu_new_lens=None):
+        """The fused operation written as its steps: positions of the new tokens, RoPE of
+        k (and q) at those positions, rounding to bf16, then kv_append of the rotated K and
+        the unchanged V.  Pools change in place; returns the rotated q (uint16) or None.
+        Tokens whose position has no table row are left out, as the library does."""
+        T_new = k_new.shape[0]
+        pos, _ = self.token_positions(context_lens, cu_new_lens, T_new)
+        ok = (pos >= 0) & (pos < rope_cos.shape[0])
+        k_rot = np.array(_u16(k_new), copy=True)
+        q_rot = None if q is None else np.array(_u16(q), copy=True)
+        if ok.any():
+            k_rot[ok] = self.round_bf16(self.rope(k_new[ok], pos[ok], rope_cos, rope_sin))
+            if q is not None:
+                q_rot[ok] = self.round_bf16(self.rope(q[ok], pos[ok], rope_cos, rope_sin))
+        if ok.all():
+            self.kv_append(k_cache, v_cache, k_rot, v_new, block_tables, context_lens,
+                           cu_new_lens)
+        else:
+            # append the tokens with a table row one at a time (the others are skipped)
+            cl = _i32(context_lens)
+            _, seq = self.token_positions(context_lens, cu_new_lens, T_new)
+            for t in np.nonzero(ok)[0]:
+                b = int(seq[t])
+                one_len = np.zeros_like(cl)
+                one_len[b] = pos[t] + 1
+                cu = np.zeros(cl.shape[0] + 1, dtype=np.int32)
+                cu[b + 1:] = 1
+                self.kv_append(k_cache, v_cache, k_rot[t:t + 1], v_new[t:t + 1], block_tables,
+                               one_len, cu)
+        return q_rot
+
 
 _default = None
 
@@ -158,3 +226,19 @@ def decode_partials(*a, **k):
 
 def lse_merge(*a, **k):
     return default().lse_merge(*a, **k)
+
+
+def token_positions(*a, **k):
+    return default().token_positions(*a, **k)
+
+
+def rope(*a, **k):
+    return default().rope(*a, **k)
+
+
+def round_bf16(*a, **k):
+    return default().round_bf16(*a, **k)
+
+
+def kv_append_rope(*a, **k):
+    return default().kv_append_rope(*a, **k)

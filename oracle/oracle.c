@@ -399,3 +399,95 @@ int oracle_lse_merge(double *out, const double *o, const double *m,
     }
     return ORACLE_OK;
 }
+
+/* ---- Rotary position embedding ------------------------------------------
+ *
+ * The pages list RoPE among the components of the model they run (README
+ * feature list and table of contents "RoPE") but print no formula.  Reading
+ * taken: the rotary embedding of that model in the layout of its
+ * Safetensors checkpoint, where the rotated pairs are (i, i + D/2): the
+ * 2-vector (x[i], x[i + D/2]) is multiplied by the rotation matrix of the
+ * position's angle,
+ *     [ cos  -sin ] [ x[i]       ]
+ *     [ sin   cos ] [ x[i + D/2] ],
+ * i.e. the complex number x[i] + i x[i + D/2] times e^(i angle).  The
+ * angle's cosine and sine are the caller's tables, indexed [pos][i]; the
+ * position of a new token is the kv_append rule above.  Arithmetic in double
+ * precision from the widened bf16 inputs and the fp32 table entries. */
+
+/* Absolute position pos[t] and sequence seq[t] of every new token t: token
+ * t of the n_b new tokens of sequence b is at context_lens[b] - n_b + t.
+ * cu_new_lens == NULL means one new token per sequence (T_new == B). */
+int oracle_token_positions(int32_t *pos, int32_t *seq, const int32_t *context_lens,
+                           const int32_t *cu_new_lens, int32_t B, int32_t T_new)
+{
+    for (int32_t b = 0; b < B; b++) {
+        int32_t first = cu_new_lens ? cu_new_lens[b] : b;
+        int32_t n = cu_new_lens ? cu_new_lens[b + 1] - cu_new_lens[b] : 1;
+        if (first < 0 || n < 0 || first + n > T_new)
+            return ORACLE_BAD_INPUT;
+        for (int32_t t = 0; t < n; t++) {
+            pos[first + t] = context_lens[b] - n + t;
+            seq[first + t] = b;
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Rotate the rows x[rows][heads][D] (bf16 bits); row r is at position
+ * pos[r].  out[rows][heads][D] receives the rotated values. */
+int oracle_rope(double *out, const uint16_t *x, const int32_t *pos, const float *cos_tab,
+                const float *sin_tab, int32_t rows, int32_t heads, int32_t D,
+                int32_t max_position)
+{
+    if (D <= 0 || D % 2 != 0)
+        return ORACLE_BAD_INPUT;
+    int32_t half = D / 2;
+    for (int32_t r = 0; r < rows; r++) {
+        if (pos[r] < 0 || pos[r] >= max_position)
+            return ORACLE_BAD_INPUT;
+        const float *cr = cos_tab + (long)pos[r] * half;
+        const float *sr = sin_tab + (long)pos[r] * half;
+        for (int32_t h = 0; h < heads; h++) {
+            const uint16_t *src = x + ((long)r * heads + h) * D;
+            double *dst = out + ((long)r * heads + h) * D;
+            for (int32_t i = 0; i < half; i++) {
+                double a = widen_bf16(src[i]), b = widen_bf16(src[i + half]);
+                double c = (double)cr[i], s = (double)sr[i];
+                dst[i] = a * c - b * s;
+                dst[i + half] = b * c + a * s;
+            }
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* Round doubles to bf16 bit patterns, to nearest with ties to even, straight
+ * from the double (no intermediate float rounding): 8 significant bits for
+ * normal values, a fixed step of 2^-133 below 2^-126, infinity past the
+ * largest finite bf16; NaN gives the quiet NaN 0x7FC0 with its sign. */
+int oracle_round_bf16(uint16_t *out, const double *x, long n)
+{
+    for (long k = 0; k < n; k++) {
+        double v = x[k];
+        uint16_t sign = signbit(v) ? 0x8000u : 0u;
+        double a = fabs(v);
+        if (isnan(v)) {
+            out[k] = (uint16_t)(sign | 0x7FC0u);
+            continue;
+        }
+        double r;
+        if (a < ldexp(1.0, -126)) {
+            r = ldexp(nearbyint(ldexp(a, 133)), -133);
+        } else {
+            int e;
+            double m = frexp(a, &e); /* a = m * 2^e, m in [0.5, 1) */
+            r = ldexp(nearbyint(ldexp(m, 8)), e - 8);
+        }
+        float f = (float)r; /* exact: at most 8 significant bits; inf past the range */
+        uint32_t u;
+        memcpy(&u, &f, sizeof u);
+        out[k] = (uint16_t)(sign | (u >> 16));
+    }
+    return ORACLE_OK;
+}

@@ -45,6 +45,18 @@ MUTANTS = [
      "int32_t j1 = j0 + partition_size - 1;"),
     ("head offset transposed", "return (((long)phys * Hkv + g) * block_size + row) * (long)D;",
      "return (((long)phys * Hkv + (Hkv - 1 - g)) * block_size + row) * (long)D;"),
+    ("rope sign flipped", "dst[i] = a * c - b * s;", "dst[i] = a * c + b * s;"),
+    ("rope cos and sin swapped", "double c = (double)cr[i], s = (double)sr[i];",
+     "double c = (double)sr[i], s = (double)cr[i];"),
+    ("rope table columns reversed", "double c = (double)cr[i], s = (double)sr[i];",
+     "double c = (double)cr[half - 1 - i], s = (double)sr[half - 1 - i];"),
+    ("rope pairs adjacent elements", "double a = widen_bf16(src[i]), b = widen_bf16(src[i + half]);",
+     "double a = widen_bf16(src[i]), b = widen_bf16(src[i ^ 1]);"),
+    ("rope position off by one", "pos[first + t] = context_lens[b] - n + t;",
+     "pos[first + t] = context_lens[b] - n + t + 1;"),
+    ("bf16 rounding through float", "double a = fabs(v);", "double a = fabs((double)(float)v);"),
+    ("bf16 rounding truncates", "r = ldexp(nearbyint(ldexp(m, 8)), e - 8);",
+     "r = ldexp(floor(ldexp(m, 8)), e - 8);"),
 ]
 
 

@@ -366,6 +366,132 @@ def pin_gqa(orc):
     assert np.array_equal(mha, out)
 
 
+# ------------------------------------------------------------------ RoPE ---
+
+def rope_tables(max_pos, D, base=10000.0):
+    """fp32 cos/sin tables [max_pos][D/2] of the angles pos * base^(-2i/D)."""
+    inv = base ** (-np.arange(D // 2, dtype=np.float64) * 2.0 / D)
+    ang = np.arange(max_pos, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+def pin_rope_turns(orc):
+    """Closed forms of the rotation of the pairs (i, i + D/2): a quarter turn
+    maps (x, y) to (-y, x), a half turn to (-x, -y), angle 0 leaves x alone,
+    and each pair takes its own table column.  An interleaved pairing, a
+    flipped sign or a misplaced column changes these exact values."""
+    import torch
+    x = torch.tensor([[[1.0, 2.0, 3.0, 4.0]]] * 4).to(torch.bfloat16)
+    x = x.view(torch.int16).numpy().view(np.uint16)
+    cos = np.array([[1, 1], [0, 0], [-1, -1], [0, 1]], dtype=np.float32)
+    sin = np.array([[0, 0], [1, 1], [0, 0], [1, 0]], dtype=np.float32)
+    out = orc.rope(x, np.arange(4, dtype=np.int32), cos, sin)
+    assert np.array_equal(out[0, 0], [1, 2, 3, 4])
+    assert np.array_equal(out[1, 0], [-3, -4, 1, 2])
+    assert np.array_equal(out[2, 0], [-1, -2, -3, -4])
+    assert np.array_equal(out[3, 0], [-3, 2, 1, 4])
+
+
+def pin_rope_is_complex_rotation(orc):
+    """RoPE of the pair (a, b) is the complex product (a + ib)(cos + i sin):
+    numpy's complex multiply of the same fp32 table entries agrees."""
+    rng = np.random.default_rng(41)
+    D, P = 16, 10
+    ang = rng.uniform(-np.pi, np.pi, (P, D // 2))
+    cos, sin = np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+    x = bits_normal(rng, (7, 3, D))
+    pos = rng.integers(0, P, 7).astype(np.int32)
+    out = orc.rope(x, pos, cos, sin)
+    xf = ref.widen(x)
+    z = (xf[..., :D // 2] + 1j * xf[..., D // 2:]) * \
+        (cos[pos].astype(np.float64) + 1j * sin[pos].astype(np.float64))[:, None, :]
+    assert np.allclose(out[..., :D // 2], z.real, rtol=0, atol=1e-12)
+    assert np.allclose(out[..., D // 2:], z.imag, rtol=0, atol=1e-12)
+
+
+def pin_rope_relative_position(orc):
+    """With angles proportional to the position, q.k after RoPE depends only
+    on the distance of the two positions (within the fp32 rounding of the
+    tables)."""
+    rng = np.random.default_rng(43)
+    D = 64
+    cos, sin = rope_tables(4096, D)
+    q, k = bits_normal(rng, (1, 1, D)), bits_normal(rng, (1, 1, D))
+    scale = float(np.linalg.norm(ref.widen(q)) * np.linalg.norm(ref.widen(k)))
+    def dot(m, n):
+        a = orc.rope(q, np.array([m], np.int32), cos, sin)
+        b = orc.rope(k, np.array([n], np.int32), cos, sin)
+        return float((a * b).sum())
+    for m, n in ((7, 3), (100, 0), (2000, 1999)):
+        base = dot(m, n)
+        for shift in (1, 17, 1000):
+            assert abs(dot(m + shift, n + shift) - base) <= 2e-5 * scale
+    # and it does depend on the distance
+    assert abs(dot(10, 0) - dot(0, 0)) > 1e-3 * scale
+
+
+def pin_token_positions(orc):
+    """New token t of the n_b new tokens of sequence b sits at
+    context_lens[b] - n_b + t (the append rule); empty sequences own none."""
+    pos, seq = orc.token_positions(np.array([10, 7, 3], np.int32),
+                                   np.array([0, 2, 2, 5], np.int32), 5)
+    assert pos.tolist() == [8, 9, 0, 1, 2] and seq.tolist() == [0, 0, 2, 2, 2]
+    pos, seq = orc.token_positions(np.array([4, 1, 9], np.int32), None, 3)
+    assert pos.tolist() == [3, 0, 8] and seq.tolist() == [0, 1, 2]
+
+
+def pin_round_bf16(orc):
+    """Rounding to bf16: torch's fp32 -> bf16 conversion (nearest even) for
+    values an fp32 holds exactly, and direct rounding of the double where an
+    intermediate fp32 would round twice."""
+    import torch
+    rng = np.random.default_rng(47)
+    vals = np.concatenate([
+        rng.standard_normal(2000).astype(np.float32),
+        (rng.standard_normal(200) * 1e-39).astype(np.float32),   # fp32 subnormals
+        np.float32([1 + 2**-8, 1 + 3 * 2**-8, -(1 + 2**-8), 3.0e38, 3.4e38, np.inf, -np.inf,
+                    0.0, -0.0, 2**-133 * 0.5, 2**-133 * 1.5])])
+    want = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(orc.round_bf16(vals.astype(np.float64)), want)
+    # above the halfway point only in the double: rounds up, not to even
+    assert orc.round_bf16(np.array([1 + 2**-8 + 2**-40]))[0] == 0x3F81
+    assert orc.round_bf16(np.array([-(1 + 2**-8 + 2**-40)]))[0] == 0xBF81
+    assert orc.round_bf16(np.array([np.nan]))[0] & 0x7FFF == 0x7FC0
+
+
+def pin_kv_append_rope_steps(orc):
+    """The fused operation stores round_bf16(rope(k)) and the unchanged v at
+    the append slots, rotates q the same way, touches no other pool byte, and
+    leaves alone a token whose position has no table row."""
+    rng = np.random.default_rng(53)
+    Hq, Hkv, D, bs, N = 4, 2, 8, 4, 12
+    cos, sin = rope_tables(12, D)
+    tables = rng.permutation(N).astype(np.int32).reshape(3, 4)
+    lens = np.array([6, 13, 3], np.int32)           # after the append
+    cu = np.array([0, 2, 5, 6], np.int32)           # 2, 3 and 1 new tokens
+    kn, vn = bits_normal(rng, (6, Hkv, D)), bits_normal(rng, (6, Hkv, D))
+    q = bits_normal(rng, (6, Hq, D))
+    k = np.full((N, Hkv, bs, D), 0x7FC1, np.uint16)
+    v = k.copy()
+    q_rot = orc.kv_append_rope(k, v, kn, vn, tables, lens, cos, sin, q, cu)
+    pos, _ = orc.token_positions(lens, cu, 6)
+    assert pos.tolist() == [4, 5, 10, 11, 12, 2]
+    ok = pos < 12                                    # position 12 has no table row
+    touched = np.zeros((N, Hkv, bs), bool)
+    for t, b in enumerate([0, 0, 1, 1, 1, 2]):
+        if not ok[t]:
+            assert np.array_equal(q_rot[t], q[t])
+            continue
+        blk, row = tables[b, pos[t] // bs], pos[t] % bs
+        kr = orc.round_bf16(orc.rope(kn[t:t + 1], pos[t:t + 1], cos, sin))[0]
+        qr = orc.round_bf16(orc.rope(q[t:t + 1], pos[t:t + 1], cos, sin))[0]
+        assert np.array_equal(k[blk, :, row], kr) and np.array_equal(v[blk, :, row], vn[t])
+        assert np.array_equal(q_rot[t], qr)
+        touched[blk, :, row] = True
+    assert (k[~touched] == 0x7FC1).all() and (v[~touched] == 0x7FC1).all()
+    assert touched.sum() == int(ok.sum()) * Hkv
+
+
 PINS = [
     pin_golden_decode, pin_golden_prefill, pin_golden_kv_append, pin_golden_merge,
     pin_context_one_returns_v, pin_identical_keys_give_mean,
@@ -374,6 +500,8 @@ PINS = [
     pin_peaked_scores, pin_shift_invariance, pin_affine_values_and_convexity,
     pin_block_size_independence, pin_batch_independence, pin_nan_outside_context,
     pin_split_merge, pin_prefill_row_is_decode, pin_kv_append_roundtrip, pin_gqa,
+    pin_rope_turns, pin_rope_is_complex_rotation, pin_rope_relative_position,
+    pin_token_positions, pin_round_bf16, pin_kv_append_rope_steps,
 ]
 NEEDS_GOLDEN = {pin_golden_decode, pin_golden_prefill, pin_golden_kv_append, pin_golden_merge}
 
