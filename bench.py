@@ -20,7 +20,10 @@ dominant kernel -- the combined append + decode kernel (the decode kernel
 with --form two-calls) -- timed with HIP events over graph replays of its 16
 calls on the stream the graph runs on.  `cpu_baseline` is the CPU oracle on
 a bounded sample of the same workload.  `prefill` reports the causal paged
-prefill workload (4 x 512 + 2 x 2048 prompts) on the bf16 MFMA roofline.
+prefill workload (4 x 512 + 2 x 2048 prompts) on the bf16 MFMA roofline, and
+`rope_append` the rotary embedding of q and k fused with the append
+(kv_append_rope) for the step's 64 new tokens and for the prefill prompts'
+6144, on the HBM roofline.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--form planned|auto|two-calls]
 """
@@ -46,6 +49,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-rope", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for counter scaling)")
     ap.add_argument("--form", choices=("planned", "auto", "two-calls"), default="planned",
@@ -154,6 +158,58 @@ def run_prefill(torch, pkv, wl, steps, warmup):
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}}
+
+
+def rope_append_bytes(T, Hq, Hkv, D):
+    """kv_append_rope: q rows read and written (when given), k_new and v_new rows read
+    and stored, and the token's cos and sin rows (D/2 fp32 each)."""
+    return T * ((Hq + 2 * Hkv) * D * 2 * 2 + 2 * (D // 2) * 4)
+
+
+def run_rope_append(torch, pkv, wl, steps, warmup, decode_args):
+    """kv_append_rope (RoPE of q and k fused with the append) for the decode step's
+    new tokens (one per sequence, decode_args = pools, tables, lens of the step) and for
+    the prefill workload's prompts (6144 new tokens); returns a dict."""
+    dev = "cuda"
+    res = {}
+    k_pool, v_pool, tables, lens, B, Hq, Hkv, D = decode_args
+    g = wl.generator(11)
+    cases = {"decode_step": (k_pool, v_pool, wl.randn_bf16(g, (B, Hkv, D)).to(dev),
+                             wl.randn_bf16(g, (B, Hkv, D)).to(dev), tables, lens, None,
+                             wl.randn_bf16(g, (B, Hq, D)).to(dev), int(lens.max()) + 1)}
+    p = wl.prefill_case()
+    cases["prefill"] = (p.k_cache.to(dev), p.v_cache.to(dev), p.k_new.to(dev),
+                        p.v_new.to(dev), p.block_tables.to(dev), p.context_lens.to(dev),
+                        p.cu_new_lens.to(dev), p.q.to(dev), int(p.context_lens.max()))
+    for name, (k, v, kn, vn, t, l, cu, q, max_pos) in cases.items():
+        cos, sin = (x.to(dev) for x in wl.rope_tables(max_pos, D))
+        def call():
+            pkv.kv_append_rope(k, v, kn, vn, t, l, cos, sin, q=q, cu_new_lens=cu)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        per_graph = 8
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(per_graph):
+                call()
+        graph.replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(steps):
+            graph.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) / (steps * per_graph) * 1e3
+        T = kn.shape[0]
+        nbytes = rope_append_bytes(T, q.shape[1], Hkv, D)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"new_tokens": T, "us_per_call": round(us, 2), "algorithmic_bytes": nbytes,
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    return res
 
 
 def main():
@@ -320,6 +376,14 @@ def main():
             result["prefill"] = run_prefill(torch, pkv, wl, max(args.steps, 10), args.warmup)
         except pkv.PagedKVError as e:
             result["prefill"] = {"error": str(e)}
+
+    if not args.no_rope:
+        try:
+            result["rope_append"] = run_rope_append(
+                torch, pkv, wl, max(args.steps, 10), args.warmup,
+                (k_layers[0], v_layers[0], tables, lens, B, case.Hq, case.Hkv, case.D))
+        except pkv.PagedKVError as e:
+            result["rope_append"] = {"error": str(e)}
 
     if not args.no_cpu_baseline:
         gbs, secs, passes = cpu_baseline(case, k_layers, v_layers)

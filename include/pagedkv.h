@@ -99,6 +99,42 @@ PKV_API int kv_append(void *k_cache, void *v_cache, const void *k_new, const voi
               int32_t D, int32_t block_size, int32_t max_blocks_per_seq,
               int32_t num_blocks, void *stream);
 
+/* kv_append_rope -- the rotary position embedding (RoPE) of the new tokens'
+ * keys, and optionally of their queries, fused with kv_append.
+ *
+ * Defined by: README feature list and table of contents "RoPE" (the model's
+ * positional encoding), with kv_append's slot rule above.  The pages name
+ * RoPE without a formula; this build takes the rotary embedding of the
+ * model they run, in the layout of its Safetensors checkpoint: for i < D/2
+ * the pair (x[i], x[i + D/2]) of a q or k row is turned by the angle of the
+ * token's absolute position pos (kv_append's rule),
+ *     y[i]       = x[i] * rope_cos[pos][i] - x[i + D/2] * rope_sin[pos][i]
+ *     y[i + D/2] = x[i + D/2] * rope_cos[pos][i] + x[i] * rope_sin[pos][i],
+ * each product and the difference rounded to fp32 (no fused multiply-add),
+ * the result rounded to bf16 (nearest even).  V rows are copied unchanged.
+ *
+ * q                 [T_new][Hq][D] bf16, rotated in place; NULL leaves the
+ *                   queries alone (Hq is then ignored).
+ * k_new, v_new      [T_new][Hkv][D] bf16; the pools receive rotated K and
+ *                   unchanged V at kv_append's slots.
+ * rope_cos, rope_sin  [max_position][D/2] fp32, the caller's angle tables
+ *                   (e.g. cos and sin of pos * inv_freq[i]; any frequency
+ *                   scheme); read-only.
+ * k_cache, v_cache, block_tables, context_lens, cu_new_lens, B, T_new, Hkv,
+ * block_size, max_blocks_per_seq, num_blocks as for kv_append.
+ * A token whose position lies outside [0, max_position) is left alone (no
+ * rotation of its q rows, no store of its K/V rows).  Rows whose slot falls
+ * outside the table or pool are not stored (their q rows are still rotated).
+ * This build implements D == 64 (PKV_ERR_UNSUPPORTED otherwise); pools, rows
+ * and tables must be 16-byte aligned.
+ */
+PKV_API int kv_append_rope(void *k_cache, void *v_cache, void *q, const void *k_new,
+                   const void *v_new, const float *rope_cos, const float *rope_sin,
+                   int32_t max_position, const int32_t *block_tables,
+                   const int32_t *context_lens, const int32_t *cu_new_lens, int32_t B,
+                   int32_t T_new, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
+                   int32_t max_blocks_per_seq, int32_t num_blocks, void *stream);
+
 /* Bytes of device workspace paged_attention_decode needs for these arguments
  * (0 when no split is requested).  Pure function of its arguments; makes no
  * HIP call.  Returns 0 for arguments decode would reject. */

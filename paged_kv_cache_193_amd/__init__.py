@@ -8,6 +8,8 @@ call raises -- there is no CPU fallback.
 Entry points (same names as the C ABI in include/pagedkv.h):
     kv_append(k_cache, v_cache, k_new, v_new, block_tables, context_lens,
               cu_new_lens=None)
+    kv_append_rope(k_cache, v_cache, k_new, v_new, block_tables, context_lens,
+              rope_cos, rope_sin, q=None, cu_new_lens=None)
     paged_attention_decode(out, q, k_cache, v_cache, block_tables,
               context_lens, scale, max_context_len, partition_size=AUTO,
               workspace=None)
@@ -37,7 +39,8 @@ PARTITION_AUTO = -1
 PARTITION_PLANNED = -2
 
 # every symbol include/pagedkv.h declares
-ABI_SYMBOLS = ("pagedkv_last_error", "kv_append", "paged_attention_decode_workspace_size",
+ABI_SYMBOLS = ("pagedkv_last_error", "kv_append", "kv_append_rope",
+               "paged_attention_decode_workspace_size",
                "paged_attention_decode", "paged_attention_decode_append",
                "paged_attention_decode_plan",
                "paged_attention_prefill_causal")
@@ -65,6 +68,8 @@ def load_library():
     lib.pagedkv_last_error.restype = ctypes.c_char_p
     lib.kv_append.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.kv_append.restype = ctypes.c_int
+    lib.kv_append_rope.argtypes = [P, P, P, P, P, P, P, I, P, P, P, I, I, I, I, I, I, I, I, P]
+    lib.kv_append_rope.restype = ctypes.c_int
     lib.paged_attention_decode_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.paged_attention_decode_workspace_size.restype = Z
     lib.paged_attention_decode.argtypes = [P, I, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I,
@@ -143,6 +148,42 @@ def kv_append(k_cache, v_cache, k_new, v_new, block_tables, context_lens, cu_new
         _dev(block_tables, torch.int32, "block_tables"),
         _dev(context_lens, torch.int32, "context_lens"), cu_ptr, B, T_new, Hkv, D, bs, maxb, N,
         _stream()))
+
+
+def kv_append_rope(k_cache, v_cache, k_new, v_new, block_tables, context_lens, rope_cos,
+                   rope_sin, q=None, cu_new_lens=None):
+    """kv_append of the RoPE-rotated new keys (k_new/v_new [T_new][Hkv][D]) and, when q
+    ([T_new][Hq][D]) is given, the same rotation of q in place.  rope_cos/rope_sin are
+    float32 [max_position][D/2] device tables."""
+    torch = _torch()
+    N, Hkv, bs, D = k_cache.shape
+    B, maxb = block_tables.shape
+    T_new = k_new.shape[0]
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(v_new.shape) != tuple(k_new.shape):
+        raise ValueError("k/v shapes differ")
+    if tuple(k_new.shape[1:]) != (Hkv, D):
+        raise ValueError("k_new must be [T_new][Hkv][D]")
+    if rope_cos.dim() != 2 or tuple(rope_sin.shape) != tuple(rope_cos.shape) or \
+            rope_cos.shape[1] * 2 != D:
+        raise ValueError("rope_cos and rope_sin must both be [max_position][D/2]")
+    q_ptr, Hq = None, 0
+    if q is not None:
+        if q.dim() != 3 or q.shape[0] != T_new or q.shape[2] != D:
+            raise ValueError("q must be [T_new][Hq][D]")
+        Hq = q.shape[1]
+        q_ptr = _dev(q, torch.bfloat16, "q")
+    cu_ptr = None
+    if cu_new_lens is not None:
+        if cu_new_lens.numel() != B + 1:
+            raise ValueError("cu_new_lens must have B+1 entries")
+        cu_ptr = _dev(cu_new_lens, torch.int32, "cu_new_lens")
+    _check(load_library().kv_append_rope(
+        _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"), q_ptr,
+        _dev(k_new, torch.bfloat16, "k_new"), _dev(v_new, torch.bfloat16, "v_new"),
+        _dev(rope_cos, torch.float32, "rope_cos"), _dev(rope_sin, torch.float32, "rope_sin"),
+        rope_cos.shape[0], _dev(block_tables, torch.int32, "block_tables"),
+        _dev(context_lens, torch.int32, "context_lens"), cu_ptr, B, T_new, Hq, Hkv, D, bs, maxb,
+        N, _stream()))
 
 
 def paged_attention_decode_workspace_size(B, Hq, Hkv, D, block_size, max_context_len,

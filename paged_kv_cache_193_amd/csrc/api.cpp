@@ -128,6 +128,38 @@ int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new
   return hip_status(pkv::launch_kv_append(a, (hipStream_t)stream), "kv_append launch");
 }
 
+int kv_append_rope(void* k_cache, void* v_cache, void* q, const void* k_new, const void* v_new,
+                   const float* rope_cos, const float* rope_sin, int32_t max_position,
+                   const int32_t* block_tables, const int32_t* context_lens,
+                   const int32_t* cu_new_lens, int32_t B, int32_t T_new, int32_t Hq,
+                   int32_t Hkv, int32_t D, int32_t block_size, int32_t max_blocks_per_seq,
+                   int32_t num_blocks, void* stream) {
+  if (B < 0 || T_new < 0)
+    return fail(PKV_ERR_INVALID_ARG, "B (%d) and T_new (%d) must be >= 0", B, T_new);
+  if (B == 0 || T_new == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_new || !v_new || !rope_cos || !rope_sin || !block_tables ||
+      !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (Hkv <= 0 || D <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 || num_blocks <= 0 ||
+      max_position <= 0)
+    return fail(PKV_ERR_INVALID_ARG,
+                "Hkv, D, block_size, max_blocks_per_seq, num_blocks, max_position must be > 0");
+  if (q && Hq <= 0) return fail(PKV_ERR_INVALID_ARG, "Hq must be > 0 when q is given (got %d)", Hq);
+  if (D != kD) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d not implemented (64 only)", D);
+  if (!cu_new_lens && T_new != B)
+    return fail(PKV_ERR_INVALID_ARG, "cu_new_lens is NULL but T_new (%d) != B (%d)", T_new, B);
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new) ||
+      !aligned16(rope_cos) || !aligned16(rope_sin) || (q && !aligned16(q)))
+    return fail(PKV_ERR_INVALID_ARG, "pools, rows and rope tables must be 16-byte aligned");
+  const int32_t hq = q ? Hq : 0;
+  if ((int64_t)T_new * (hq + 2 * (int64_t)Hkv) * 4 / 256 >= INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "too many new rows for one launch");
+  pkv::RopeAppendArgs a{k_cache, v_cache, q, k_new, v_new, rope_cos, rope_sin, block_tables,
+                        context_lens, cu_new_lens, max_position, B, T_new, hq, Hkv, block_size,
+                        max_blocks_per_seq, num_blocks};
+  return hip_status(pkv::launch_kv_append_rope(a, (hipStream_t)stream), "kv_append_rope launch");
+}
+
 size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                              int32_t block_size, int32_t max_context_len,
                                              int32_t partition_size) {

@@ -77,4 +77,115 @@ hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// kv_append_rope: the rotary position embedding of each new token's keys
+// (and, when q is given, of its queries, in place) fused with the append
+// above.  The pages list RoPE among the model's components (README feature
+// list and table of contents "RoPE") without a formula; the reading here is
+// the rotary embedding of the model they run, loaded from its Safetensors
+// checkpoint: for i < D/2 the pair (x[i], x[i + D/2]) is turned by the angle
+// whose cosine and sine the caller's tables hold for the token's position,
+//     y[i]       = x[i] cos - x[i + D/2] sin
+//     y[i + D/2] = x[i + D/2] cos + x[i] sin,
+// each product and the difference rounded to fp32 (no fused multiply-add),
+// then to bf16 (nearest even).  The position is the token's absolute
+// position, the same one the append uses for its slot.
+//
+// One thread per (token, row, quarter c): rows are the Hq query heads (when
+// q is given), then the Hkv key heads, then the Hkv value heads.  A thread
+// owns elements [8c, 8c + 8) and [32 + 8c, 32 + 8c + 8) of its row, i.e. both
+// halves of 8 rotation pairs: two 16-byte loads, two 16-byte stores, and the
+// matching 32 bytes of cos and of sin.  A token's rows are consecutive, so
+// every wavefront reads and writes whole 128-byte rows.
+__global__ void __launch_bounds__(256)
+kv_append_rope_kernel(RopeAppendArgs a) {
+  constexpr int kHalf = 32;  // D / 2, D == 64
+  const int rows = a.Hq + 2 * a.Hkv;
+  const int64_t per_token = (int64_t)rows * 4;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)a.T_new * per_token) return;
+  const int t = (int)(gid / per_token);
+  const int rem = (int)(gid - (int64_t)t * per_token);
+  const int r = rem >> 2, c = rem & 3;
+
+  int b, first, n;
+  if (a.cu_new_lens == nullptr) {
+    b = t;
+    first = t;
+    n = 1;
+  } else {
+    int lo = 0, hi = a.B;  // invariant: cu[lo] <= t < cu[hi]
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (a.cu_new_lens[mid] <= t) lo = mid; else hi = mid;
+    }
+    b = lo;
+    first = a.cu_new_lens[b];
+    n = a.cu_new_lens[b + 1] - first;
+  }
+  const int pos = a.context_lens[b] - n + (t - first);
+  if (pos < 0 || pos >= a.max_position) return;  // no angle for it: leave the token alone
+
+  const bool is_q = r < a.Hq;
+  const bool is_v = r >= a.Hq + a.Hkv;
+  const uint16_t* src;
+  uint16_t* dst;
+  if (is_q) {
+    dst = static_cast<uint16_t*>(a.q) + ((int64_t)t * a.Hq + r) * 64;
+    src = dst;
+  } else {
+    const int h = is_v ? r - a.Hq - a.Hkv : r - a.Hq;
+    const int logical_block = pos / a.block_size;
+    if (logical_block >= a.max_blocks_per_seq) return;
+    const int phys = a.block_tables[(int64_t)b * a.max_blocks_per_seq + logical_block];
+    if (phys < 0 || phys >= a.num_blocks) return;
+    const int row = pos - logical_block * a.block_size;
+    src = static_cast<const uint16_t*>(is_v ? a.v_new : a.k_new) + ((int64_t)t * a.Hkv + h) * 64;
+    dst = static_cast<uint16_t*>(is_v ? a.v_cache : a.k_cache) +
+          (((int64_t)phys * a.Hkv + h) * a.block_size + row) * 64;
+  }
+  u32x4 lo = *reinterpret_cast<const u32x4*>(src + 8 * c);
+  u32x4 hi = *reinterpret_cast<const u32x4*>(src + kHalf + 8 * c);
+  if (!is_v) {
+    const float* cr = a.rope_cos + (int64_t)pos * kHalf + 8 * c;
+    const float* sr = a.rope_sin + (int64_t)pos * kHalf + 8 * c;
+    const float4 c0 = *reinterpret_cast<const float4*>(cr);
+    const float4 c1 = *reinterpret_cast<const float4*>(cr + 4);
+    const float4 s0 = *reinterpret_cast<const float4*>(sr);
+    const float4 s1 = *reinterpret_cast<const float4*>(sr + 4);
+    const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    const float sn[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    u32x4 lo2, hi2;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float y0[2], y1[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+#pragma clang fp contract(off)
+        const uint32_t bx = e ? (lo[w] & 0xFFFF0000u) : (lo[w] << 16);
+        const uint32_t by = e ? (hi[w] & 0xFFFF0000u) : (hi[w] << 16);
+        const float x = __builtin_bit_cast(float, bx);
+        const float y = __builtin_bit_cast(float, by);
+        const float co = cs[2 * w + e], si = sn[2 * w + e];
+        const float xc = x * co, ys = y * si, yc = y * co, xs = x * si;
+        y0[e] = xc - ys;
+        y1[e] = yc + xs;
+      }
+      lo2[w] = pack_bf16(y0[0], y0[1]);
+      hi2[w] = pack_bf16(y1[0], y1[1]);
+    }
+    lo = lo2;
+    hi = hi2;
+  }
+  *reinterpret_cast<u32x4*>(dst + 8 * c) = lo;
+  *reinterpret_cast<u32x4*>(dst + kHalf + 8 * c) = hi;
+}
+
+hipError_t launch_kv_append_rope(const RopeAppendArgs& a, hipStream_t stream) {
+  const int64_t total = (int64_t)a.T_new * (a.Hq + 2 * a.Hkv) * 4;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(kv_append_rope_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace pkv

@@ -20,6 +20,22 @@ struct KvAppendArgs {
 };
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 
+// kv_append with the rotary embedding of the new keys (and queries), D == 64.
+struct RopeAppendArgs {
+  void* k_cache;
+  void* v_cache;
+  void* q;  // [T_new][Hq][D], rotated in place, or nullptr (then Hq == 0)
+  const void* k_new;
+  const void* v_new;
+  const float* rope_cos;  // [max_position][D/2]
+  const float* rope_sin;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* cu_new_lens;
+  int32_t max_position, B, T_new, Hq, Hkv, block_size, max_blocks_per_seq, num_blocks;
+};
+hipError_t launch_kv_append_rope(const RopeAppendArgs& a, hipStream_t stream);
+
 // Decode work decomposition (see decode.hip).
 enum DecodeMode : int { kWhole = 0, kFixed = 1, kAuto = 2 };
 

@@ -33,6 +33,10 @@ import torch
 
 HQ, HKV, HEAD_DIM, BLOCK_SIZE = 32, 8, 64, 16
 SCALE = 0.125  # 1 / sqrt(64)
+# Base of the rotary frequencies in the synthetic angle tables (the value of
+# the Llama 3 family; its long-context frequency scaling is left out: the
+# library takes whatever tables the caller builds).
+ROPE_BASE = 500000.0
 
 CONFIGS = {
     "tiny": dict(B=1, Hq=4, Hkv=1, num_blocks=8, lens=("fixed", 37), seed=1),
@@ -131,6 +135,14 @@ class PagedCase:
     @property
     def max_context_len(self) -> int:
         return int(self.context_lens.max()) if len(self.context_lens) else 0
+
+
+def rope_tables(max_position: int, D: int = HEAD_DIM, base: float = ROPE_BASE):
+    """Angle tables for the rotary embedding: fp32 cos and sin [max_position][D/2]
+    of pos * base^(-2i/D), computed in float64 and rounded once."""
+    inv = base ** (-torch.arange(D // 2, dtype=torch.float64) * 2.0 / D)
+    ang = torch.arange(max_position, dtype=torch.float64)[:, None] * inv[None, :]
+    return torch.cos(ang).to(torch.float32), torch.sin(ang).to(torch.float32)
 
 
 def poison_unused(case: PagedCase, value=float("nan")) -> None:

@@ -196,6 +196,40 @@ def test_append_nothing_to_do(lib):
     assert append_call(lib, B=0, T=0) == pkv.PKV_OK
 
 
+def rope_call(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, q=FAKE, kn=FAKE, vn=FAKE, cos=FAKE, sin=FAKE, maxpos=4096, bt=FAKE,
+             cl=FAKE, cu=None, B=2, T=2, Hq=32, Hkv=8, D=64, bs=16, maxb=4, N=8, stream=None)
+    a.update(kw)
+    return lib.kv_append_rope(a["k"], a["v"], a["q"], a["kn"], a["vn"], a["cos"], a["sin"],
+                              a["maxpos"], a["bt"], a["cl"], a["cu"], a["B"], a["T"], a["Hq"],
+                              a["Hkv"], a["D"], a["bs"], a["maxb"], a["N"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(T=-3), pkv.PKV_ERR_INVALID_ARG),
+    (dict(k=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(cos=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(sin=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(T=5), pkv.PKV_ERR_INVALID_ARG),      # no cu_new_lens but T_new != B
+    (dict(maxpos=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(Hq=0), pkv.PKV_ERR_INVALID_ARG),     # q given without query heads
+    (dict(D=128), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(bs=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(q=ctypes.c_void_p(0x1008)), pkv.PKV_ERR_INVALID_ARG),
+    (dict(cos=ctypes.c_void_p(0x1004)), pkv.PKV_ERR_INVALID_ARG),
+])
+def test_append_rope_rejects(lib, kw, code):
+    assert rope_call(lib, **kw) == code
+
+
+def test_append_rope_nothing_to_do(lib):
+    assert rope_call(lib, T=0, cu=FAKE) == pkv.PKV_OK
+    assert rope_call(lib, B=0, T=0) == pkv.PKV_OK
+    # without q the query head count is not looked at (still rejected for D)
+    assert rope_call(lib, q=None, Hq=0, D=128) == pkv.PKV_ERR_UNSUPPORTED
+
+
 def prefill_call(lib, **kw):
     a = dict(out=FAKE, out_dtype=pkv.PKV_OUT_F32, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE,
              cu=FAKE, B=2, T=20, Hq=32, Hkv=8, D=64, bs=16, maxb=4, N=8, maxq=10, scale=0.125,
