@@ -135,6 +135,78 @@ PKV_API int kv_append_rope(void *k_cache, void *v_cache, void *q, const void *k_
                    int32_t T_new, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_size,
                    int32_t max_blocks_per_seq, int32_t num_blocks, void *stream);
 
+/* ---- Host control plane: block allocator and continuous-batching scheduler.
+ *
+ * Defined by: guide ch. 4 "PagedAttention" (KV pages handed out on demand by
+ * a block allocator, against up-front reservations whose fragmentation wastes
+ * 60-80% of the memory) and ch. 5 "The Scheduler" (continuous batching:
+ * requests join and leave the running batch at every step); digest "Core
+ * Mechanics" (continuous batching).  Host code only: no HIP call, no device
+ * memory.  A scheduler object is not thread safe.
+ *
+ * Policy (the pages print none): every step schedules the running sequences
+ * oldest first (one token each once decoding, the next prompt chunk while in
+ * prefill), then waiting requests in arrival order while the batch
+ * (max_batch rows), the token budget (max_step_tokens) and the free blocks
+ * allow; prompts beyond the budget are processed in chunks over several
+ * steps.  When a running sequence needs a block and none is free, the most
+ * recently arrived running sequence not yet in this step's batch gives up
+ * its blocks and waits again (it recomputes its tokens when readmitted).
+ * static_batching != 0 instead admits up to max_batch requests only when the
+ * running set is empty (the comparison the guide draws).
+ */
+typedef struct pkv_scheduler pkv_scheduler;
+
+/* Number of int64 counters pkv_sched_stats writes:
+ *   0 steps            1 tokens scheduled        2 prefill tokens (incl. recomputed)
+ *   3 decode tokens    4 preemptions             5 requests finished
+ *   6 free blocks now  7 running now             8 waiting now
+ *   9  sum over steps of the cached tokens of the running sequences
+ *   10 sum over steps of the slots in their blocks (paged allocation)
+ *   11 sum over steps of prompt + max_new - 1 per running sequence (a static
+ *      reservation of each request's own maximum)
+ *   12 sum over steps of max_blocks_per_seq * block_size per running sequence
+ *      (a static reservation of the longest sequence allowed)
+ *   13 sum over steps of the batch rows                                   */
+#define PKV_SCHED_STATS 16
+
+/* New scheduler over physical blocks 0..num_blocks-1 (all free); NULL for a
+ * non-positive argument or out of host memory. */
+PKV_API pkv_scheduler *pkv_sched_create(int32_t num_blocks, int32_t block_size,
+                                int32_t max_blocks_per_seq, int32_t max_batch,
+                                int32_t max_step_tokens, int32_t static_batching);
+PKV_API void pkv_sched_destroy(pkv_scheduler *s);
+
+/* Queue request `id` (unique among unfinished requests) with prompt_len prompt
+ * tokens that will sample max_new_tokens tokens.  PKV_ERR_UNSUPPORTED if its
+ * longest cached length (prompt_len + max_new_tokens - 1) needs more blocks
+ * than a table row or the pool holds. */
+PKV_API int pkv_sched_add_request(pkv_scheduler *s, int64_t id, int32_t prompt_len,
+                          int32_t max_new_tokens);
+
+/* Plan one engine step and advance the sequences as if it ran.  Returns the
+ * batch size B >= 0 (or a negative status) and fills host arrays of at least
+ * max_batch rows: seq_ids[B]; q_lens[B], the tokens of each sequence this step
+ * stores and attends with (1 when decoding); context_lens[B], its cached
+ * tokens after this step's append; cu_q_lens[B+1], prefix sums of q_lens;
+ * block_tables[B][max_blocks_per_seq], its physical blocks in logical order,
+ * -1 past the last.  These are the arguments kv_append (cu_new_lens =
+ * cu_q_lens) and paged_attention_prefill_causal take; a batch of decoding
+ * sequences alone fits paged_attention_decode.  Blocks of finished or
+ * preempted sequences are reused from the next step on (or, for preempted
+ * ones, later in the same step by other sequences), so steps must execute in
+ * order on one stream. */
+PKV_API int pkv_sched_step(pkv_scheduler *s, int64_t *seq_ids, int32_t *q_lens,
+                   int32_t *context_lens, int32_t *cu_q_lens, int32_t *block_tables);
+
+/* Requests that finished (which == 0) or were preempted (which == 1) in the
+ * last step: returns their count and writes up to max_ids of them. */
+PKV_API int32_t pkv_sched_events(const pkv_scheduler *s, int32_t which, int64_t *ids,
+                         int32_t max_ids);
+
+/* Counters (PKV_SCHED_STATS int64 values, see above) into out. */
+PKV_API int pkv_sched_stats(const pkv_scheduler *s, int64_t *out);
+
 /* Bytes of device workspace paged_attention_decode needs for these arguments
  * (0 when no split is requested).  Pure function of its arguments; makes no
  * HIP call.  Returns 0 for arguments decode would reject. */

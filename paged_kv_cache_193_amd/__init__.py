@@ -21,6 +21,8 @@ Entry points (same names as the C ABI in include/pagedkv.h):
     paged_attention_decode_plan(k_cache, block_tables, context_lens, Hq,
               max_context_len, workspace)
     paged_attention_decode_workspace_size(...)
+    Scheduler(num_blocks, block_size, max_blocks_per_seq, max_batch, max_step_tokens,
+              static_batching=False)  -- pkv_sched_* (host control plane)
 """
 import ctypes
 import os
@@ -43,7 +45,15 @@ ABI_SYMBOLS = ("pagedkv_last_error", "kv_append", "kv_append_rope",
                "paged_attention_decode_workspace_size",
                "paged_attention_decode", "paged_attention_decode_append",
                "paged_attention_decode_plan",
-               "paged_attention_prefill_causal")
+               "paged_attention_prefill_causal",
+               "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_add_request",
+               "pkv_sched_step", "pkv_sched_events", "pkv_sched_stats")
+
+PKV_SCHED_STATS = 16
+SCHED_STAT_NAMES = ("steps", "tokens", "prefill_tokens", "decode_tokens", "preemptions",
+                    "finished", "free_blocks", "running", "waiting", "cached_token_steps",
+                    "paged_slot_steps", "static_request_slot_steps", "static_max_slot_steps",
+                    "batch_row_steps")
 
 _lib = None
 
@@ -83,6 +93,19 @@ def load_library():
     lib.paged_attention_prefill_causal.argtypes = [P, I, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                    I, I, F, P]
     lib.paged_attention_prefill_causal.restype = ctypes.c_int
+    L = ctypes.c_int64
+    lib.pkv_sched_create.argtypes = [I, I, I, I, I, I]
+    lib.pkv_sched_create.restype = P
+    lib.pkv_sched_destroy.argtypes = [P]
+    lib.pkv_sched_destroy.restype = None
+    lib.pkv_sched_add_request.argtypes = [P, L, I, I]
+    lib.pkv_sched_add_request.restype = ctypes.c_int
+    lib.pkv_sched_step.argtypes = [P, P, P, P, P, P]
+    lib.pkv_sched_step.restype = ctypes.c_int
+    lib.pkv_sched_events.argtypes = [P, I, P, I]
+    lib.pkv_sched_events.restype = ctypes.c_int32
+    lib.pkv_sched_stats.argtypes = [P, P]
+    lib.pkv_sched_stats.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -275,6 +298,78 @@ def paged_attention_prefill_causal(out, q, k_cache, v_cache, block_tables, conte
         _dev(context_lens, torch.int32, "context_lens"),
         _dev(cu_q_lens, torch.int32, "cu_q_lens"), B, T, Hq, Hkv, D, bs, maxb, N,
         int(max_q_len), float(scale), _stream()))
+
+
+class Scheduler:
+    """Host block allocator + continuous-batching scheduler of libpagedkv.so
+    (pkv_sched_*).  step() returns the next engine step as numpy arrays ready
+    for the kernels: seq_ids [B], q_lens [B], context_lens [B], cu_q_lens
+    [B+1] and block_tables [B][max_blocks_per_seq] (int32, -1 past the last
+    block)."""
+
+    def __init__(self, num_blocks, block_size, max_blocks_per_seq, max_batch,
+                 max_step_tokens, static_batching=False):
+        import numpy as np
+        self._np = np
+        self._lib = load_library()
+        self.max_batch, self.max_blocks_per_seq = max_batch, max_blocks_per_seq
+        self._h = self._lib.pkv_sched_create(num_blocks, block_size, max_blocks_per_seq,
+                                             max_batch, max_step_tokens,
+                                             1 if static_batching else 0)
+        if not self._h:
+            raise ValueError("pkv_sched_create: every size must be positive")
+        self._ids = np.zeros(max_batch, dtype=np.int64)
+        self._q = np.zeros(max_batch, dtype=np.int32)
+        self._ctx = np.zeros(max_batch, dtype=np.int32)
+        self._cu = np.zeros(max_batch + 1, dtype=np.int32)
+        self._tab = np.zeros((max_batch, max_blocks_per_seq), dtype=np.int32)
+
+    def close(self):
+        if self._h:
+            self._lib.pkv_sched_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:  # noqa: BLE001 - interpreter shutdown
+            pass
+
+    def add_request(self, rid, prompt_len, max_new_tokens):
+        rc = self._lib.pkv_sched_add_request(self._h, int(rid), int(prompt_len),
+                                             int(max_new_tokens))
+        if rc != PKV_OK:
+            raise PagedKVError(rc, f"request {rid}: prompt {prompt_len}, max_new "
+                               f"{max_new_tokens} rejected")
+
+    def step(self):
+        p = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+        B = self._lib.pkv_sched_step(self._h, p(self._ids), p(self._q), p(self._ctx),
+                                     p(self._cu), p(self._tab))
+        if B < 0:
+            raise PagedKVError(B, "pkv_sched_step")
+        return dict(seq_ids=self._ids[:B].copy(), q_lens=self._q[:B].copy(),
+                    context_lens=self._ctx[:B].copy(), cu_q_lens=self._cu[:B + 1].copy(),
+                    block_tables=self._tab[:B].copy())
+
+    def _events(self, which):
+        n = self._lib.pkv_sched_events(self._h, which, None, 0)
+        out = self._np.zeros(max(n, 1), dtype=self._np.int64)
+        self._lib.pkv_sched_events(self._h, which, out.ctypes.data_as(ctypes.c_void_p), n)
+        return out[:n].tolist()
+
+    def finished(self):
+        """Requests that finished in the last step."""
+        return self._events(0)
+
+    def preempted(self):
+        """Requests preempted (blocks released, requeued) in the last step."""
+        return self._events(1)
+
+    def stats(self):
+        out = self._np.zeros(PKV_SCHED_STATS, dtype=self._np.int64)
+        _check(self._lib.pkv_sched_stats(self._h, out.ctypes.data_as(ctypes.c_void_p)))
+        return {k: int(out[i]) for i, k in enumerate(SCHED_STAT_NAMES)}
 
 
 def decode_workspace(B, Hq, Hkv, D, block_size, max_context_len, partition_size, device):

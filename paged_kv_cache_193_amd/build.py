@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libpagedkv.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "pagedkv")
-SOURCES = ["api.cpp", "kv_append.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "scheduler.cpp", "kv_append.hip", "decode.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 COMMON = [
