@@ -49,10 +49,11 @@ class Oracle:
         lib.oracle_token_positions.argtypes = [P, P, P, P, I, I]
         lib.oracle_rope.argtypes = [P, P, P, P, P, I, I, I, I]
         lib.oracle_round_bf16.argtypes = [P, P, ctypes.c_long]
+        lib.oracle_copy_blocks.argtypes = [P, P, P, P, I, I, I, I, I]
         for f in (lib.oracle_kv_append, lib.oracle_decode, lib.oracle_decode_online,
                   lib.oracle_prefill_causal, lib.oracle_decode_partials,
                   lib.oracle_lse_merge, lib.oracle_token_positions, lib.oracle_rope,
-                  lib.oracle_round_bf16):
+                  lib.oracle_round_bf16, lib.oracle_copy_blocks):
             f.restype = ctypes.c_int
         self.lib = lib
         self.path = path
@@ -163,6 +164,15 @@ class Oracle:
         self.lib.oracle_round_bf16(_ptr(out), _ptr(xd), xd.size)
         return out
 
+    def copy_blocks(self, k_cache, v_cache, src, dst):
+        """Block dst[i] of both uint16 pools [N][Hkv][bs][D] gets block src[i], in place."""
+        assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+        N, Hkv, bs, D = k_cache.shape
+        s, d = _i32(src), _i32(dst)
+        rc = self.lib.oracle_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(s), _ptr(d), len(s),
+                                         Hkv, bs, D, N)
+        _check(rc, "copy_blocks")
+
     def kv_append_rope(self, k_cache, v_cache, k_new, v_new, block_tables, context_lens,
                        rope_cos, rope_sin, q=None, cu_new_lens=None):
         """The fused operation written as its steps: positions of the new tokens, RoPE of
@@ -242,3 +252,7 @@ def round_bf16(*a, **k):
 
 def kv_append_rope(*a, **k):
     return default().kv_append_rope(*a, **k)
+
+
+def copy_blocks(*a, **k):
+    return default().copy_blocks(*a, **k)

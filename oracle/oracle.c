@@ -491,3 +491,24 @@ int oracle_round_bf16(uint16_t *out, const double *x, long n)
     }
     return ORACLE_OK;
 }
+
+/* ---- Block copies (copy on write of shared blocks) ------------------------
+ * The guide's ch. 7 ("Prefix Caching") shares KV blocks between sequences;
+ * a sequence about to write into a shared block first gets its own copy.
+ * Block dst[i] of both pools receives the bytes of block src[i] (every KV
+ * head and row), in pair order. */
+int oracle_copy_blocks(uint16_t *k_cache, uint16_t *v_cache, const int32_t *src,
+                       const int32_t *dst, int32_t n_pairs, int32_t Hkv, int32_t block_size,
+                       int32_t D, int32_t num_blocks)
+{
+    long per_block = (long)Hkv * block_size * D;
+    for (int32_t i = 0; i < n_pairs; i++) {
+        if (src[i] < 0 || src[i] >= num_blocks || dst[i] < 0 || dst[i] >= num_blocks)
+            return ORACLE_BAD_INPUT;
+        memcpy(k_cache + dst[i] * per_block, k_cache + src[i] * per_block,
+               (size_t)per_block * sizeof(uint16_t));
+        memcpy(v_cache + dst[i] * per_block, v_cache + src[i] * per_block,
+               (size_t)per_block * sizeof(uint16_t));
+    }
+    return ORACLE_OK;
+}

@@ -57,6 +57,10 @@ MUTANTS = [
     ("bf16 rounding through float", "double a = fabs(v);", "double a = fabs((double)(float)v);"),
     ("bf16 rounding truncates", "r = ldexp(nearbyint(ldexp(m, 8)), e - 8);",
      "r = ldexp(floor(ldexp(m, 8)), e - 8);"),
+    ("block copy reversed", "memcpy(k_cache + dst[i] * per_block, k_cache + src[i] * per_block,",
+     "memcpy(k_cache + src[i] * per_block, k_cache + dst[i] * per_block,"),
+    ("block copy skips V", "memcpy(v_cache + dst[i] * per_block, v_cache + src[i] * per_block,",
+     "memcpy(v_cache + dst[i] * per_block, v_cache + dst[i] * per_block,"),
 ]
 
 

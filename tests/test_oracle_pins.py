@@ -492,6 +492,26 @@ def pin_kv_append_rope_steps(orc):
     assert touched.sum() == int(ok.sum()) * Hkv
 
 
+def pin_copy_blocks(orc):
+    """Copy on write: the destination block holds the source's bytes in both
+    pools afterwards, every other byte keeps its value, and pairs apply in
+    order (a copy of a copy carries the first source)."""
+    rng = np.random.default_rng(59)
+    k = bits_normal(rng, (6, 2, 4, 8))
+    v = bits_normal(rng, (6, 2, 4, 8))
+    k0, v0 = k.copy(), v.copy()
+    orc.copy_blocks(k, v, [4, 1, 2], [0, 5, 3])
+    assert np.array_equal(k[0], k0[4]) and np.array_equal(v[0], v0[4])
+    assert np.array_equal(k[5], k0[1]) and np.array_equal(v[5], v0[1])
+    assert np.array_equal(k[3], k0[2]) and np.array_equal(v[3], v0[2])
+    for blk in (1, 2, 4):
+        assert np.array_equal(k[blk], k0[blk]) and np.array_equal(v[blk], v0[blk])
+    orc.copy_blocks(k, v, [0, 3], [1, 0])
+    assert np.array_equal(k[1], k0[4]) and np.array_equal(k[0], k0[2])
+    with pytest.raises(ValueError):
+        orc.copy_blocks(k, v, [6], [0])
+
+
 PINS = [
     pin_golden_decode, pin_golden_prefill, pin_golden_kv_append, pin_golden_merge,
     pin_context_one_returns_v, pin_identical_keys_give_mean,
@@ -501,7 +521,7 @@ PINS = [
     pin_block_size_independence, pin_batch_independence, pin_nan_outside_context,
     pin_split_merge, pin_prefill_row_is_decode, pin_kv_append_roundtrip, pin_gqa,
     pin_rope_turns, pin_rope_is_complex_rotation, pin_rope_relative_position,
-    pin_token_positions, pin_round_bf16, pin_kv_append_rope_steps,
+    pin_token_positions, pin_round_bf16, pin_kv_append_rope_steps, pin_copy_blocks,
 ]
 NEEDS_GOLDEN = {pin_golden_decode, pin_golden_prefill, pin_golden_kv_append, pin_golden_merge}
 
