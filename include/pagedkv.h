@@ -99,6 +99,21 @@ PKV_API int kv_append(void *k_cache, void *v_cache, const void *k_new, const voi
               int32_t D, int32_t block_size, int32_t max_blocks_per_seq,
               int32_t num_blocks, void *stream);
 
+/* kv_copy_blocks -- copy whole pool blocks (every KV head and row of K and
+ * of V): block dst_blocks[i] receives block src_blocks[i], for the copies on
+ * write a scheduler step lists (guide ch. 7: shared prefix blocks are copied
+ * before one of their sequences writes into them).
+ *
+ * src_blocks, dst_blocks  [n_pairs] int32 device arrays; pairs whose ids lie
+ *                   outside [0, num_blocks) are skipped.  A destination must
+ *                   not also be a source or another pair's destination.
+ * k_cache, v_cache  pools as for kv_append, written in place.  Bit-exact.
+ * D % 8 == 0; pools 16-byte aligned.  n_pairs == 0 is a no-op.
+ */
+PKV_API int kv_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_blocks,
+                   const int32_t *dst_blocks, int32_t n_pairs, int32_t Hkv, int32_t D,
+                   int32_t block_size, int32_t num_blocks, void *stream);
+
 /* kv_append_rope -- the rotary position embedding (RoPE) of the new tokens'
  * keys, and optionally of their queries, fused with kv_append.
  *
@@ -151,7 +166,8 @@ PKV_API int kv_append_rope(void *k_cache, void *v_cache, void *q, const void *k_
  * allow; prompts beyond the budget are processed in chunks over several
  * steps.  When a running sequence needs a block and none is free, the most
  * recently arrived running sequence not yet in this step's batch gives up
- * its blocks and waits again (it recomputes its tokens when readmitted).
+ * its blocks and waits again (it recomputes its tokens when readmitted); a
+ * step that preempted admits no waiting request.
  * static_batching != 0 instead admits up to max_batch requests only when the
  * running set is empty (the comparison the guide draws).
  */
@@ -167,7 +183,9 @@ typedef struct pkv_scheduler pkv_scheduler;
  *      reservation of each request's own maximum)
  *   12 sum over steps of max_blocks_per_seq * block_size per running sequence
  *      (a static reservation of the longest sequence allowed)
- *   13 sum over steps of the batch rows                                   */
+ *   13 sum over steps of the batch rows
+ *   14 block copies on write                15 prompt tokens taken from a
+ *                                              shared prefix instead of computed */
 #define PKV_SCHED_STATS 16
 
 /* New scheduler over physical blocks 0..num_blocks-1 (all free); NULL for a
@@ -183,6 +201,31 @@ PKV_API void pkv_sched_destroy(pkv_scheduler *s);
  * than a table row or the pool holds. */
 PKV_API int pkv_sched_add_request(pkv_scheduler *s, int64_t id, int32_t prompt_len,
                           int32_t max_new_tokens);
+
+/* As pkv_sched_add_request, for a request whose first prefix_len prompt tokens
+ * (a positive multiple of block_size, below prompt_len) are those of the live
+ * sequence prefix_owner (guide ch. 7 "Prefix Caching").  When admitted while
+ * that sequence holds them computed, the request shares their blocks (each
+ * block's count of tables goes up) and computes only the rest; otherwise it
+ * computes everything.  The caller guarantees the tokens are the same. */
+PKV_API int pkv_sched_add_request_prefix(pkv_scheduler *s, int64_t id, int32_t prompt_len,
+                                 int32_t max_new_tokens, int64_t prefix_owner,
+                                 int32_t prefix_len);
+
+/* Start sequence child_id from the running sequence parent_id, which must be
+ * decoding (every token but its latest sample cached): the child has the same
+ * history and shares every block of it, its latest sample is its own, and it
+ * samples extra_tokens more tokens (several samples of one prompt).  The first
+ * store of either into their shared partly filled block copies that block
+ * first (pkv_sched_copies). */
+PKV_API int pkv_sched_fork(pkv_scheduler *s, int64_t parent_id, int64_t child_id,
+                   int32_t extra_tokens);
+
+/* Block copies the last step needs before its appends (copy on write):
+ * returns their count and writes up to max_pairs (source, destination) block
+ * ids, to be executed with kv_copy_blocks before the step's kv_append. */
+PKV_API int32_t pkv_sched_copies(const pkv_scheduler *s, int32_t *src_blocks,
+                         int32_t *dst_blocks, int32_t max_pairs);
 
 /* Plan one engine step and advance the sequences as if it ran.  Returns the
  * batch size B >= 0 (or a negative status) and fills host arrays of at least

@@ -41,19 +41,20 @@ PARTITION_AUTO = -1
 PARTITION_PLANNED = -2
 
 # every symbol include/pagedkv.h declares
-ABI_SYMBOLS = ("pagedkv_last_error", "kv_append", "kv_append_rope",
+ABI_SYMBOLS = ("pagedkv_last_error", "kv_append", "kv_append_rope", "kv_copy_blocks",
                "paged_attention_decode_workspace_size",
                "paged_attention_decode", "paged_attention_decode_append",
                "paged_attention_decode_plan",
                "paged_attention_prefill_causal",
                "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_add_request",
-               "pkv_sched_step", "pkv_sched_events", "pkv_sched_stats")
+               "pkv_sched_step", "pkv_sched_events", "pkv_sched_stats",
+               "pkv_sched_add_request_prefix", "pkv_sched_fork", "pkv_sched_copies")
 
 PKV_SCHED_STATS = 16
 SCHED_STAT_NAMES = ("steps", "tokens", "prefill_tokens", "decode_tokens", "preemptions",
                     "finished", "free_blocks", "running", "waiting", "cached_token_steps",
                     "paged_slot_steps", "static_request_slot_steps", "static_max_slot_steps",
-                    "batch_row_steps")
+                    "batch_row_steps", "block_copies", "shared_prefix_tokens")
 
 _lib = None
 
@@ -80,6 +81,8 @@ def load_library():
     lib.kv_append.restype = ctypes.c_int
     lib.kv_append_rope.argtypes = [P, P, P, P, P, P, P, I, P, P, P, I, I, I, I, I, I, I, I, P]
     lib.kv_append_rope.restype = ctypes.c_int
+    lib.kv_copy_blocks.argtypes = [P, P, P, P, I, I, I, I, I, P]
+    lib.kv_copy_blocks.restype = ctypes.c_int
     lib.paged_attention_decode_workspace_size.argtypes = [I, I, I, I, I, I, I]
     lib.paged_attention_decode_workspace_size.restype = Z
     lib.paged_attention_decode.argtypes = [P, I, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I,
@@ -106,6 +109,12 @@ def load_library():
     lib.pkv_sched_events.restype = ctypes.c_int32
     lib.pkv_sched_stats.argtypes = [P, P]
     lib.pkv_sched_stats.restype = ctypes.c_int
+    lib.pkv_sched_add_request_prefix.argtypes = [P, L, I, I, L, I]
+    lib.pkv_sched_add_request_prefix.restype = ctypes.c_int
+    lib.pkv_sched_fork.argtypes = [P, L, L, I]
+    lib.pkv_sched_fork.restype = ctypes.c_int
+    lib.pkv_sched_copies.argtypes = [P, P, P, I]
+    lib.pkv_sched_copies.restype = ctypes.c_int32
     _lib = lib
     return lib
 
@@ -171,6 +180,23 @@ def kv_append(k_cache, v_cache, k_new, v_new, block_tables, context_lens, cu_new
         _dev(block_tables, torch.int32, "block_tables"),
         _dev(context_lens, torch.int32, "context_lens"), cu_ptr, B, T_new, Hkv, D, bs, maxb, N,
         _stream()))
+
+
+def kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks):
+    """Copy pool block src_blocks[i] onto dst_blocks[i] (int32 device tensors), K and V."""
+    torch = _torch()
+    N, Hkv, bs, D = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k/v shapes differ")
+    n = src_blocks.numel()
+    if dst_blocks.numel() != n:
+        raise ValueError("src_blocks and dst_blocks differ in length")
+    if n == 0:
+        return
+    _check(load_library().kv_copy_blocks(
+        _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
+        _dev(src_blocks, torch.int32, "src_blocks"), _dev(dst_blocks, torch.int32, "dst_blocks"),
+        n, Hkv, D, bs, N, _stream()))
 
 
 def kv_append_rope(k_cache, v_cache, k_new, v_new, block_tables, context_lens, rope_cos,
@@ -335,12 +361,34 @@ class Scheduler:
         except Exception:  # noqa: BLE001 - interpreter shutdown
             pass
 
-    def add_request(self, rid, prompt_len, max_new_tokens):
-        rc = self._lib.pkv_sched_add_request(self._h, int(rid), int(prompt_len),
-                                             int(max_new_tokens))
+    def add_request(self, rid, prompt_len, max_new_tokens, prefix_owner=None, prefix_len=0):
+        """Queue a request; with prefix_owner, its first prefix_len tokens are the
+        owner's and their blocks are shared when it is admitted."""
+        if prefix_owner is None:
+            rc = self._lib.pkv_sched_add_request(self._h, int(rid), int(prompt_len),
+                                                 int(max_new_tokens))
+        else:
+            rc = self._lib.pkv_sched_add_request_prefix(self._h, int(rid), int(prompt_len),
+                                                        int(max_new_tokens), int(prefix_owner),
+                                                        int(prefix_len))
         if rc != PKV_OK:
             raise PagedKVError(rc, f"request {rid}: prompt {prompt_len}, max_new "
                                f"{max_new_tokens} rejected")
+
+    def fork(self, parent, child, extra_tokens):
+        """Start `child` from the decoding sequence `parent`, sharing its blocks."""
+        rc = self._lib.pkv_sched_fork(self._h, int(parent), int(child), int(extra_tokens))
+        if rc != PKV_OK:
+            raise PagedKVError(rc, f"fork {parent} -> {child} rejected")
+
+    def copies(self):
+        """(src, dst) int32 arrays of the block copies the last step needs first."""
+        n = self._lib.pkv_sched_copies(self._h, None, None, 0)
+        src = self._np.zeros(max(n, 1), dtype=self._np.int32)
+        dst = self._np.zeros(max(n, 1), dtype=self._np.int32)
+        self._lib.pkv_sched_copies(self._h, src.ctypes.data_as(ctypes.c_void_p),
+                                   dst.ctypes.data_as(ctypes.c_void_p), n)
+        return src[:n], dst[:n]
 
     def step(self):
         p = lambda a: a.ctypes.data_as(ctypes.c_void_p)

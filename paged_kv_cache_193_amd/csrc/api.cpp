@@ -128,6 +128,25 @@ int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new
   return hip_status(pkv::launch_kv_append(a, (hipStream_t)stream), "kv_append launch");
 }
 
+int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks,
+                   const int32_t* dst_blocks, int32_t n_pairs, int32_t Hkv, int32_t D,
+                   int32_t block_size, int32_t num_blocks, void* stream) {
+  if (n_pairs < 0) return fail(PKV_ERR_INVALID_ARG, "n_pairs must be >= 0 (got %d)", n_pairs);
+  if (n_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !src_blocks || !dst_blocks)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (Hkv <= 0 || D <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "Hkv, D, block_size, num_blocks must be > 0");
+  if (D % 8 != 0) return fail(PKV_ERR_UNSUPPORTED, "D %d is not a multiple of 8", D);
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "pools must be 16-byte aligned");
+  if ((int64_t)n_pairs * 2 * Hkv * block_size * (D / 8) / 256 >= INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "too many block copies for one launch");
+  pkv::CopyBlocksArgs a{k_cache, v_cache, src_blocks, dst_blocks, n_pairs, Hkv, D, block_size,
+                        num_blocks};
+  return hip_status(pkv::launch_kv_copy_blocks(a, (hipStream_t)stream), "kv_copy_blocks launch");
+}
+
 int kv_append_rope(void* k_cache, void* v_cache, void* q, const void* k_new, const void* v_new,
                    const float* rope_cos, const float* rope_sin, int32_t max_position,
                    const int32_t* block_tables, const int32_t* context_lens,

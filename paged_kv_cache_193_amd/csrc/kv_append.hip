@@ -65,6 +65,38 @@ kv_append_kernel(uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
   *reinterpret_cast<u32x4*>(d + dst) = *reinterpret_cast<const u32x4*>(s + src);
 }
 
+// kv_copy_blocks: thread id -> (pair, plane K or V, 16-byte chunk of the
+// block); consecutive threads copy consecutive chunks of one block.
+__global__ void __launch_bounds__(256)
+kv_copy_blocks_kernel(uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
+                      const int32_t* __restrict__ src_blocks,
+                      const int32_t* __restrict__ dst_blocks, int32_t n_pairs,
+                      int64_t chunks_per_block, int32_t num_blocks) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_pair = 2 * chunks_per_block;
+  if (gid >= (int64_t)n_pairs * per_pair) return;
+  const int pair = (int)(gid / per_pair);
+  const int64_t rem = gid - (int64_t)pair * per_pair;
+  const int plane = rem >= chunks_per_block;
+  const int64_t chunk = plane ? rem - chunks_per_block : rem;
+  const int src = src_blocks[pair], dst = dst_blocks[pair];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  uint16_t* pool = plane ? v_cache : k_cache;
+  const u32x4 x = *reinterpret_cast<const u32x4*>(pool + (src * chunks_per_block + chunk) * 8);
+  *reinterpret_cast<u32x4*>(pool + (dst * chunks_per_block + chunk) * 8) = x;
+}
+
+hipError_t launch_kv_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream) {
+  const int64_t chunks = (int64_t)a.Hkv * a.block_size * (a.D / 8);
+  const int64_t total = (int64_t)a.n_pairs * 2 * chunks;
+  const int threads = 256;
+  const int64_t blocks = (total + threads - 1) / threads;
+  hipLaunchKernelGGL(kv_copy_blocks_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
+                     (uint16_t*)a.k_cache, (uint16_t*)a.v_cache, a.src_blocks, a.dst_blocks,
+                     a.n_pairs, chunks, a.num_blocks);
+  return hipGetLastError();
+}
+
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream) {
   const int64_t total = (int64_t)a.T_new * 2 * a.Hkv * (a.D / 8);
   const int threads = 256;

@@ -20,6 +20,16 @@ struct KvAppendArgs {
 };
 hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream);
 
+// Whole-block copies between pool blocks (copy on write of shared blocks).
+struct CopyBlocksArgs {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* src_blocks;
+  const int32_t* dst_blocks;
+  int32_t n_pairs, Hkv, D, block_size, num_blocks;
+};
+hipError_t launch_kv_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
+
 // kv_append with the rotary embedding of the new keys (and queries), D == 64.
 struct RopeAppendArgs {
   void* k_cache;

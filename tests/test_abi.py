@@ -230,6 +230,29 @@ def test_append_rope_nothing_to_do(lib):
     assert rope_call(lib, q=None, Hq=0, D=128) == pkv.PKV_ERR_UNSUPPORTED
 
 
+def copy_call(lib, **kw):
+    a = dict(k=FAKE, v=FAKE, src=FAKE, dst=FAKE, n=3, Hkv=8, D=64, bs=16, N=8, stream=None)
+    a.update(kw)
+    return lib.kv_copy_blocks(a["k"], a["v"], a["src"], a["dst"], a["n"], a["Hkv"], a["D"],
+                              a["bs"], a["N"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=-1), pkv.PKV_ERR_INVALID_ARG),
+    (dict(src=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(k=None), pkv.PKV_ERR_INVALID_ARG),
+    (dict(N=0), pkv.PKV_ERR_INVALID_ARG),
+    (dict(D=60), pkv.PKV_ERR_UNSUPPORTED),
+    (dict(v=ctypes.c_void_p(0x1004)), pkv.PKV_ERR_INVALID_ARG),
+])
+def test_copy_blocks_rejects(lib, kw, code):
+    assert copy_call(lib, **kw) == code
+
+
+def test_copy_blocks_nothing_to_do(lib):
+    assert copy_call(lib, n=0, src=None, dst=None) == pkv.PKV_OK
+
+
 def prefill_call(lib, **kw):
     a = dict(out=FAKE, out_dtype=pkv.PKV_OUT_F32, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE,
              cu=FAKE, B=2, T=20, Hq=32, Hkv=8, D=64, bs=16, maxb=4, N=8, maxq=10, scale=0.125,

@@ -78,3 +78,90 @@ def test_scheduled_steps_match_oracle():
     st = s.stats()
     assert st["finished"] == len(requests) and st["free_blocks"] == N
     s.close()
+
+
+def test_shared_blocks_through_kernels():
+    """Forks (several samples of one prompt) and requests that share a
+    prompt prefix with a live sequence: shared blocks are read by several
+    tables, each step's copies on write run (kv_copy_blocks) before its
+    appends, and every step still matches the oracle, which applies the same
+    copies to its pools."""
+    rng = np.random.default_rng(21)
+    N, bs, maxb, Hq, Hkv, D = 40, 16, 16, 32, 8, 64
+    s = pkv.Scheduler(N, bs, maxb, max_batch=8, max_step_tokens=128)
+    k = torch.full((N, Hkv, bs, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    v = torch.full_like(k, float("nan"))
+    k_host, v_host = u16(k.cpu()).copy(), u16(v.cpu()).copy()
+    g = wl.generator(23)
+    live, next_id, added, copies = set(), 0, 0, 0
+    for rid in range(3):
+        s.add_request(rid, int(rng.integers(40, 120)), int(rng.integers(10, 30)))
+        next_id, added = rid + 1, added + 1
+    done = 0
+    for step in range(2000):
+        b = s.step()
+        B = len(b["seq_ids"])
+        src, dst = s.copies()
+        done += len(s.finished())
+        if B == 0 and done == added:
+            break
+        if len(src):
+            copies += len(src)
+            pkv.kv_copy_blocks(k, v, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
+            oracle.copy_blocks(k_host, v_host, src, dst)
+        if B:
+            q_lens, lens, cu, tables = (b["q_lens"], b["context_lens"], b["cu_q_lens"],
+                                        b["block_tables"])
+            T = int(cu[-1])
+            kn, vn = wl.randn_bf16(g, (T, Hkv, D)), wl.randn_bf16(g, (T, Hkv, D))
+            q = wl.randn_bf16(g, (T, Hq, D))
+            t_d, l_d, cu_d = (torch.from_numpy(x).cuda() for x in (tables, lens, cu))
+            pkv.kv_append(k, v, kn.cuda(), vn.cuda(), t_d, l_d, cu_d)
+            out = torch.empty((T, Hq, D), dtype=torch.float32, device="cuda")
+            pkv.paged_attention_prefill_causal(out, q.cuda(), k, v, t_d, l_d, cu_d, 0.125,
+                                               int(q_lens.max()))
+            oracle.kv_append(k_host, v_host, u16(kn), u16(vn), tables, lens, cu)
+            ref = oracle.prefill_causal(u16(q), k_host, v_host, tables, lens, cu, 0.125)
+            torch.cuda.synchronize()
+            assert_close(out.cpu().numpy(), ref, f"step {step} (B={B}, T={T})")
+        live |= set(b["seq_ids"].tolist())
+        live -= set(s.finished()) | set(s.preempted())
+        # new work: forks of decoding sequences and requests sharing a prefix
+        if next_id < 24 and live:
+            parent = int(rng.choice(sorted(live)))
+            if rng.random() < 0.5:
+                try:
+                    s.fork(parent, next_id, int(rng.integers(3, 15)))
+                    added += 1
+                except pkv.PagedKVError:
+                    pass
+            else:
+                s.add_request(next_id, int(rng.integers(40, 140)), int(rng.integers(3, 15)),
+                              prefix_owner=parent, prefix_len=32)
+                added += 1
+            next_id += 1
+    else:
+        raise AssertionError("scheduler did not finish")
+    st = s.stats()
+    print(f"  {step} steps, {added} requests, {copies} block copies, "
+          f"{st['shared_prefix_tokens']} prefix tokens shared", flush=True)
+    assert np.array_equal(u16(k.cpu()), k_host) and np.array_equal(u16(v.cpu()), v_host)
+    assert copies > 0 and st["shared_prefix_tokens"] > 0
+    assert st["finished"] == added and st["free_blocks"] == N
+    s.close()
+
+
+def test_copy_blocks_bit_exact():
+    """kv_copy_blocks against the oracle's byte copy, with pairs outside the
+    pool skipped on the GPU (the oracle is given only the valid pairs)."""
+    N, Hkv, bs, D = 12, 8, 16, 64
+    g = wl.generator(29)
+    k0, v0 = wl.randn_bf16(g, (N, Hkv, bs, D)), wl.randn_bf16(g, (N, Hkv, bs, D))
+    src = np.array([3, 7, 0, 99, 11], dtype=np.int32)
+    dst = np.array([5, 1, 9, 2, -1], dtype=np.int32)
+    k, v = k0.cuda(), v0.cuda()
+    pkv.kv_copy_blocks(k, v, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
+    kh, vh = u16(k0).copy(), u16(v0).copy()
+    oracle.copy_blocks(kh, vh, src[:3], dst[:3])
+    torch.cuda.synchronize()
+    assert np.array_equal(u16(k.cpu()), kh) and np.array_equal(u16(v.cpu()), vh)

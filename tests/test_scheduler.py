@@ -178,3 +178,136 @@ def test_rejects():
         pkv.Scheduler(0, 16, 4, 2, 64)
     lib = pkv.load_library()
     assert lib.pkv_sched_step(None, None, None, None, None, None) == pkv.PKV_ERR_INVALID_ARG
+
+
+# ------------------------------------------------------- shared blocks ---
+
+def live_tables(table, preempted, finished):
+    for rid in list(preempted) + list(finished):
+        table.pop(rid, None)
+
+
+def check_shared_step(s, b, table, bs, num_blocks):
+    """Sharing-aware checks of one step: tables kept by prefix (except a
+    copied tail), every block the step writes is held by exactly one live
+    table, and the distinct live blocks plus the free list cover the pool."""
+    src, dst = s.copies()
+    copied = dict(zip(dst.tolist(), src.tolist()))
+    for row, rid in enumerate(b["seq_ids"].tolist()):
+        c, q = int(b["context_lens"][row]), int(b["q_lens"][row])
+        blocks = b["block_tables"][row, :-(-c // bs)].copy()
+        if rid in table:
+            old = table[rid]
+            for j, blk in enumerate(old):
+                # same block, or a private copy of it made this step
+                assert blocks[j] == blk or copied.get(int(blocks[j])) == blk
+        table[rid] = blocks
+    live_tables(table, s.preempted(), s.finished())
+    holders = {}
+    for rid, blocks in table.items():
+        for blk in blocks.tolist():
+            holders.setdefault(blk, set()).add(rid)
+    for row, rid in enumerate(b["seq_ids"].tolist()):
+        if rid not in table:
+            continue                      # finished in this step
+        c, q = int(b["context_lens"][row]), int(b["q_lens"][row])
+        for j in range((c - q) // bs, -(-c // bs)):
+            assert holders[int(b["block_tables"][row, j])] == {rid}, "write into a shared block"
+    assert len(holders) + s.stats()["free_blocks"] == num_blocks
+    return len(src)
+
+
+def test_fork_shares_blocks_and_copies_on_write():
+    s = pkv.Scheduler(32, 16, 8, 4, 256)
+    s.add_request(0, 40, 20)           # 40 prompt tokens: blocks 0, 1 full, block 2 partly
+    table = {}
+    b = s.step()                        # prefill
+    check_shared_step(s, b, table, 16, 32)
+    s.fork(0, 1, 10)
+    assert s.stats()["free_blocks"] == 32 - 3           # the child holds the same 3 blocks
+    b = s.step()                        # both decode into the shared partly filled block
+    n_copies = check_shared_step(s, b, table, 16, 32)
+    assert n_copies == 1                # the parent copies first; the child then owns the original
+    t0, t1 = table[0], table[1]
+    assert np.array_equal(t0[:2], t1[:2]) and t0[2] != t1[2]
+    assert s.stats()["free_blocks"] == 32 - 4
+    for _ in range(40):
+        b = s.step()
+        if len(b["seq_ids"]) == 0:
+            break
+        assert check_shared_step(s, b, table, 16, 32) == 0
+    st = s.stats()
+    assert st["finished"] == 2 and st["free_blocks"] == 32 and st["block_copies"] == 1
+    with pytest.raises(pkv.PagedKVError):
+        s.fork(0, 2, 5)                 # the parent is gone
+    s.close()
+
+
+def test_prefix_shares_whole_blocks():
+    s = pkv.Scheduler(64, 16, 16, 4, 512)
+    s.add_request(0, 100, 30)
+    table = {}
+    check_shared_step(s, s.step(), table, 16, 64)    # owner's prompt is computed
+    s.add_request(1, 90, 5, prefix_owner=0, prefix_len=64)
+    b = s.step()
+    check_shared_step(s, b, table, 16, 64)
+    row = b["seq_ids"].tolist().index(1)
+    assert int(b["q_lens"][row]) == 26 and int(b["context_lens"][row]) == 90
+    assert np.array_equal(table[1][:4], table[0][:4])
+    st = s.stats()
+    assert st["shared_prefix_tokens"] == 64 and st["prefill_tokens"] == 100 + 26
+    for _ in range(100):
+        b = s.step()
+        if len(b["seq_ids"]) == 0:
+            break
+        check_shared_step(s, b, table, 16, 64)
+    assert s.stats()["free_blocks"] == 64 and s.stats()["finished"] == 2
+    # a prefix whose owner is gone is computed in full
+    s.add_request(2, 50, 2, prefix_owner=0, prefix_len=32)
+    b = s.step()
+    assert int(b["q_lens"][0]) == 50
+    with pytest.raises(pkv.PagedKVError):
+        s.add_request(3, 50, 2, prefix_owner=2, prefix_len=20)   # not whole blocks
+    s.close()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_random_sharing_workloads(seed):
+    """Forks and shared prefixes under memory pressure: every step keeps
+    written blocks private and the pool accounted for; everything finishes."""
+    rng = np.random.default_rng(100 + seed)
+    bs, N = 16, int(rng.integers(24, 64))
+    s = pkv.Scheduler(N, bs, 24, int(rng.integers(2, 10)), int(rng.integers(64, 400)))
+    table, next_id, n_req = {}, 0, 0
+    for step in range(5000):
+        if next_id < 40 and rng.random() < 0.4:
+            live = [r for r in table]
+            if live and rng.random() < 0.5:
+                owner = int(rng.choice(live))
+                try:
+                    s.add_request(next_id, int(rng.integers(40, 200)), int(rng.integers(1, 30)),
+                                  prefix_owner=owner, prefix_len=32)
+                    n_req += 1
+                except pkv.PagedKVError:
+                    pass
+            else:
+                s.add_request(next_id, int(rng.integers(5, 200)), int(rng.integers(1, 40)))
+                n_req += 1
+            next_id += 1
+        b = s.step()
+        check_shared_step(s, b, table, bs, N)
+        if table and rng.random() < 0.2 and next_id < 40:
+            parent = int(rng.choice(list(table)))
+            try:
+                s.fork(parent, next_id, int(rng.integers(1, 20)))
+                table[next_id] = table[parent].copy()
+                n_req += 1
+            except pkv.PagedKVError:
+                pass                     # parent not decoding right now
+            next_id += 1
+        st = s.stats()
+        if next_id >= 40 and st["running"] == 0 and st["waiting"] == 0:
+            break
+    st = s.stats()
+    assert st["finished"] == n_req and st["free_blocks"] == N
+    s.close()
