@@ -187,3 +187,27 @@ def test_shared_workspace_reused_across_calls(partition):
             assert_close(out.cpu().numpy(), ref, f"reuse p={partition} rep={rep} B={c.B}")
             counters = ws[:32768 * 4].view(torch.int32)
             assert int(counters.abs().sum()) == 0
+
+
+def test_largest_batch_of_the_automatic_split():
+    """B = 4096 sequences (32768 streams, the automatic split's limit) with
+    short ragged contexts, some empty: automatic and planned splits against
+    the oracle on every row."""
+    B, maxb = 4096, 3
+    g = wl.generator(61)
+    lens = torch.randint(0, 41, (B,), generator=g, dtype=torch.int32)
+    N = int(wl.blocks_needed(lens, 16).sum()) + 1
+    tables = wl.tables_from_permutation(g, lens, 16, N, maxb, filler=N - 1)
+    q = wl.randn_bf16(g, (B, 32, 64))
+    k_cache, v_cache = wl.randn_bf16(g, (N, 8, 16, 64)), wl.randn_bf16(g, (N, 8, 16, 64))
+    ref = oracle.decode(u16(q), u16(k_cache), u16(v_cache), tables.numpy(), lens.numpy(), 0.125)
+    k, v, qd, t, l = dev(k_cache), dev(v_cache), dev(q), dev(tables), dev(lens)
+    for mode in (pkv.PARTITION_AUTO, pkv.PARTITION_PLANNED):
+        ws = pkv.decode_workspace(B, 32, 8, 64, 16, 40, mode, "cuda")
+        if mode == pkv.PARTITION_PLANNED:
+            pkv.paged_attention_decode_plan(k, t, l, 32, 40, ws)
+        out = torch.full((B, 32, 64), float("nan"), dtype=torch.float32, device="cuda")
+        pkv.paged_attention_decode(out, qd, k, v, t, l, 0.125, 40, mode, ws)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), ref, f"B=4096 mode={mode}")
+        assert int(ws[:32768 * 4].view(torch.int32).abs().sum()) == 0   # counters left at zero

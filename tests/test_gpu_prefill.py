@@ -122,3 +122,15 @@ def test_repeatable_bits():
     a = gpu_prefill(p, k, v)
     b = gpu_prefill(p, k, v)
     assert torch.equal(a, b)
+
+
+def test_long_prompt_sampled_rows():
+    """One 8192-token prompt (128 query tiles, the longest causal range here)
+    checked on sampled rows across the whole prompt."""
+    p = wl.prefill_case(prompts=[8192], num_blocks=600, seed=67)
+    k, v, kr, vr = appended(p)
+    out = gpu_prefill(p, k, v)
+    rows = [0, 1, 63, 64, 65, 2047, 4096, 6000, 8127, 8128, 8190, 8191]
+    ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
+                                p.cu_q_lens.numpy(), p.scale, rows=rows)
+    assert_close(out.cpu().numpy()[rows], ref[rows], "8192-token prompt, sampled rows")
