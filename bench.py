@@ -23,7 +23,10 @@ a bounded sample of the same workload.  `prefill` reports the causal paged
 prefill workload (4 x 512 + 2 x 2048 prompts) on the bf16 MFMA roofline, and
 `rope_append` the rotary embedding of q and k fused with the append
 (kv_append_rope) for the step's 64 new tokens and for the prefill prompts'
-6144, on the HBM roofline.
+6144, on the HBM roofline.  `long_context` times the long-context split
+workload (4 sequences of 32768 tokens) with fixed 512-token partitions merged
+by log-sum-exp, with the balanced split, and with the balanced split's plan
+(made once, outside the timed calls), on the HBM roofline.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--form planned|auto|two-calls]
 """
@@ -50,6 +53,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-rope", action="store_true")
+    ap.add_argument("--no-long", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for counter scaling)")
     ap.add_argument("--form", choices=("planned", "auto", "two-calls"), default="planned",
@@ -158,6 +162,59 @@ def run_prefill(torch, pkv, wl, steps, warmup):
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}}
+
+
+def run_long_context(torch, pkv, wl, steps, warmup, copies=4):
+    """Long-context split decode: 4 sequences of 32768 tokens, the query of each
+    attending to its whole context, with fixed 512-token partitions merged by
+    log-sum-exp (partition_size = 512), with the balanced split, and with the
+    balanced split's plan (made once: the lengths and tables do not change).  `copies`
+    pool pairs (256 MiB each per pool) are used in turn so that the 256 MB
+    last-level cache does not hold the previous call's blocks; returns a dict."""
+    dev = "cuda"
+    case = wl.device_decode_case("long", dev, layers=copies)
+    k_layers, v_layers = case.extra["k_layers"], case.extra["v_layers"]
+    B, Hq, Hkv, D = case.B, case.Hq, case.Hkv, case.D
+    t, l, q = case.block_tables.to(dev), case.context_lens.to(dev), case.q.to(dev)
+    max_ctx = case.max_context_len
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    dec_b = decode_bytes(case.context_lens.tolist(), B, Hq, Hkv, D, 2)
+    res = {"workload": "long-context split decode: batch 4, context 32768 each, 32q/8kv "
+                       "heads, head_dim 64, block_size 16, 16384-block pool",
+           "algorithmic_bytes": dec_b}
+    for name, part in (("partition_512", 512), ("auto", pkv.PARTITION_AUTO),
+                       ("planned", pkv.PARTITION_PLANNED)):
+        ws = pkv.decode_workspace(B, Hq, Hkv, D, 16, max_ctx, part, dev)
+        if part == pkv.PARTITION_PLANNED:  # lengths and tables stay fixed: plan once
+            pkv.paged_attention_decode_plan(k_layers[0], t, l, Hq, max_ctx, ws)
+
+        def calls():
+            for c in range(copies):
+                pkv.paged_attention_decode(out, q, k_layers[c], v_layers[c], t, l,
+                                           case.scale, max_ctx, part, ws)
+        for _ in range(warmup):
+            calls()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            calls()
+        graph.replay()
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(steps):
+            graph.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        us = ev0.elapsed_time(ev1) / (steps * copies) * 1e3
+        gbs = dec_b / (us * 1e-6) / 1e9
+        res[name] = {"us_per_call": round(us, 2),
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    del case, k_layers, v_layers
+    torch.cuda.empty_cache()
+    return res
 
 
 def rope_append_bytes(T, Hq, Hkv, D):
@@ -376,6 +433,13 @@ def main():
             result["prefill"] = run_prefill(torch, pkv, wl, max(args.steps, 10), args.warmup)
         except pkv.PagedKVError as e:
             result["prefill"] = {"error": str(e)}
+
+    if not args.no_long:
+        try:
+            result["long_context"] = run_long_context(torch, pkv, wl, max(args.steps, 10),
+                                                      args.warmup)
+        except pkv.PagedKVError as e:
+            result["long_context"] = {"error": str(e)}
 
     if not args.no_rope:
         try:

@@ -117,24 +117,40 @@ __device__ __forceinline__ int eff_ctx(const Params& p, int b) {
   return c > p.ctx_cap ? p.ctx_cap : c;
 }
 
-// Issue the four 16-byte loads of block `j` of the stream, whose physical id
-// `phys` was read earlier; returns the number of valid tokens in the block
-// (0 when `phys` is not a valid block id: then block 0 is read and ignored).
-__device__ __forceinline__ int issue_block(BlockRegs& r, const Params& p, int phys, int g,
-                                           int j, int ctx, int lane_off) {
+// Issue the two 16-byte K loads of block `j` of the stream, whose physical id
+// `phys` was read earlier; `ub` receives the block's element offset for the
+// matching V loads (issue_v).  Returns the number of valid tokens in the
+// block (0 when `phys` is not a valid block id: then block 0 is read and
+// ignored).
+__device__ __forceinline__ int issue_k(BlockRegs& r, const Params& p, int phys, int g, int j,
+                                       int ctx, int lane_off, int64_t& ub) {
   int nv = ctx - j * kBS;
   nv = nv > kBS ? kBS : nv;
   if (phys < 0 || phys >= p.num_blocks) {
     phys = 0;
     nv = 0;
   }
-  const int64_t base = ((int64_t)phys * p.Hkv + g) * (kBS * kD) + lane_off;
-  const uint16_t* kp = p.k_cache + base;
-  const uint16_t* vp = p.v_cache + base;
+  ub = ((int64_t)phys * p.Hkv + g) * (kBS * kD);
+  const uint16_t* kp = p.k_cache + ub + lane_off;
   r.ka = *reinterpret_cast<const u32x4*>(kp);
   r.kb = *reinterpret_cast<const u32x4*>(kp + 8 * kD);
+  return nv;
+}
+
+// The two 16-byte V loads of the block whose K issue_k issued.
+__device__ __forceinline__ void issue_v(BlockRegs& r, const Params& p, int64_t ub,
+                                        int lane_off) {
+  const uint16_t* vp = p.v_cache + ub + lane_off;
   r.va = *reinterpret_cast<const u32x4*>(vp);
   r.vb = *reinterpret_cast<const u32x4*>(vp + 8 * kD);
+}
+
+// All four loads of a block at once (first group of a segment).
+__device__ __forceinline__ int issue_block(BlockRegs& r, const Params& p, int phys, int g,
+                                           int j, int ctx, int lane_off) {
+  int64_t ub;
+  const int nv = issue_k(r, p, phys, g, j, ctx, lane_off, ub);
+  issue_v(r, p, ub, lane_off);
   return nv;
 }
 
@@ -202,10 +218,12 @@ __device__ __forceinline__ void block_pv(LaneState& st, const BlockRegs& r, floa
 // The blocks go through a ring of kRing register slots in groups of kRing:
 // the scores of a whole group are formed first, the running max moves once
 // per group (one rescale of the accumulator, no branch), then P.V runs block
-// by block and each slot is refilled with the block kRing ahead as soon as its
-// V is consumed.  Every group issues exactly kRing block loads (past the
-// segment end the last block is re-read, a cache hit marked invalid), so the
-// hardware wait counts stay exact.
+// by block.  Each slot is refilled with the block kRing ahead in two halves:
+// its K as soon as the group's scores are formed, its V as soon as its own
+// P.V is done, so the next group's loads are in flight while this group is
+// scored and while it is accumulated.  Every group issues exactly kRing
+// block loads (past the segment end the last block is re-read, a cache hit
+// marked invalid), so the hardware wait counts stay exact.
 __device__ __forceinline__ void run_segment(LaneState& st, const Params& p, int b, int g,
                                             int j0, int j1, int ctx, int lane) {
   const int grp = lane >> 3, i = lane & 7;
@@ -241,6 +259,7 @@ __device__ __forceinline__ void run_segment(LaneState& st, const Params& p, int 
 
   BlockRegs ring[kRing];
   int nvalid[kRing];
+  int64_t ub[kRing];  // element offsets of the slots' blocks, for their V loads
 #pragma unroll
   for (int s = 0; s < kRing; ++s) {
     const int j = j0 + s < last ? j0 + s : last;
@@ -258,6 +277,24 @@ __device__ __forceinline__ void run_segment(LaneState& st, const Params& p, int 
     for (int s = 0; s < kRing; ++s) {
       x[s] = block_score(ring[s], qv, p.scale_log2, quad1);
       if (!full && own_tok >= nvalid[s]) x[s] = -INFINITY;
+    }
+    // the K halves of the slots are free: refill them with the blocks kRing
+    // ahead (their V halves follow each slot's P.V)
+    int nv_next[kRing];
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+      const int jn = j0 + base + s + kRing;
+      const int j = jn < last ? jn : last;
+      if (j - tab_base >= 64) {
+        tab_base += 64;
+        tab = trow[tab_base + lane < last ? tab_base + lane : last];
+        // wait here (vmcnt 0), inside the branch, so the common path after it
+        // carries no wait for this load
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+      const int nv = issue_k(ring[s], p, __builtin_amdgcn_readlane(tab, j - tab_base), g, j, ctx,
+                             lane_off, ub[s]);
+      nv_next[s] = jn < j1 ? nv : 0;
     }
     // one max per group, shared by the mirror pair (same head, tokens t, t+8)
     float mx = x[0];
@@ -287,19 +324,8 @@ __device__ __forceinline__ void run_segment(LaneState& st, const Params& p, int 
         block_pv<false>(st, ring[s], pw, quad1, true, true);
       else
         block_pv<true>(st, ring[s], pw, quad1, grp < nvalid[s], grp + 8 < nvalid[s]);
-      // refill this slot with the block kRing ahead
-      const int jn = j0 + base + s + kRing;
-      const int j = jn < last ? jn : last;
-      if (j - tab_base >= 64) {
-        tab_base += 64;
-        tab = trow[tab_base + lane < last ? tab_base + lane : last];
-        // wait here (vmcnt 0), inside the branch, so the common path after it
-        // carries no wait for this load
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-      }
-      const int nv = issue_block(ring[s], p, __builtin_amdgcn_readlane(tab, j - tab_base), g, j,
-                                 ctx, lane_off);
-      nvalid[s] = jn < j1 ? nv : 0;
+      issue_v(ring[s], p, ub[s], lane_off);
+      nvalid[s] = nv_next[s];
     }
   }
 }
@@ -851,6 +877,7 @@ decode_auto_kernel(Params p) {
   const int lane_off = grp * kD + 8 * i;
   BlockRegs ring[kRing];
   int nvalid[kRing];
+  int64_t ub[kRing];  // element offsets of the slots' blocks, for their V loads
   bool slast[kRing];  // append: the slot holds its stream's last block
   int sphys[kRing];   // append: that block's physical id
   uint32_t qv[4][4], qn[4][4];
@@ -1029,20 +1056,15 @@ decode_auto_kernel(Params p) {
     if (kAppend) {
       knv = knn;
       vnv = vnn;
-      // the new token's row replaces the one loaded from the pools, and is
-      // stored there (lanes grp == t % 8 hold token t in ka/va or kb/vb)
+      // the new token's row replaces the one loaded from the pools (its K
+      // here, its V before the slot's P.V), and is stored there (lanes
+      // grp == t % 8 hold token t in ka/va or kb/vb)
 #pragma unroll
       for (int s = 0; s < kRing; ++s) {
         if (slast[s] && s_newok[cc.b]) {
           const int t = (cc.ctx - 1) & (kBS - 1);
-          if (grp == t) {
-            ring[s].ka = knv;
-            ring[s].va = vnv;
-          }
-          if (grp + 8 == t) {
-            ring[s].kb = knv;
-            ring[s].vb = vnv;
-          }
+          if (grp == t) ring[s].ka = knv;
+          if (grp + 8 == t) ring[s].kb = knv;
           if (grp == (t & 7)) {
             const int64_t off = (((int64_t)sphys[s] * p.Hkv + cc.g) * kBS + t) * kD + 8 * i;
             *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_cache) + off) = knv;
@@ -1060,6 +1082,25 @@ decode_auto_kernel(Params p) {
     for (int s = 0; s < kRing; ++s) {
       x[s] = block_score(ring[s], qv, p.scale_log2, quad1);
       if (!full && own_tok >= nvalid[s]) x[s] = -INFINITY;
+    }
+    // q, the new rows and the K halves of the group at ci go out now (a
+    // re-read when none is left), so they are in flight while this group is
+    // accumulated; each slot's V half follows its P.V
+    load_q(qn, p, ci.b, ci.g, i, c);
+    if (kAppend) load_new(knn, vnn, p, ci.b, ci.g, i);
+    int nv_next[kRing];
+    bool slast_next[kRing];
+    int sphys_next[kRing];
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+      const int j = ci.j + s < ci.nbr - 1 ? ci.j + s : ci.nbr - 1;
+      const int id = __builtin_amdgcn_readlane(tab, (int)(xr - win) + s);
+      const int nv = issue_k(ring[s], p, id, ci.g, j, ci.ctx, lane_off, ub[s]);
+      nv_next[s] = ci.j + s < ci.nbr ? nv : 0;
+      if (kAppend) {
+        slast_next[s] = ci.j + s == ci.nbr - 1 && nv > 0;
+        sphys_next[s] = id;
+      }
     }
     float mx = x[0];
 #pragma unroll
@@ -1083,22 +1124,20 @@ decode_auto_kernel(Params p) {
     for (int s = 0; s < kRing; ++s) {
       const float pw = __builtin_amdgcn_exp2f(x[s] - m_use);
       st.l += pw;
+      if (kAppend && slast[s] && s_newok[cc.b]) {
+        const int t = (cc.ctx - 1) & (kBS - 1);
+        if (grp == t) ring[s].va = vnv;
+        if (grp + 8 == t) ring[s].vb = vnv;
+      }
       if (full)
         block_pv<false>(st, ring[s], pw, quad1, true, true);
       else
         block_pv<true>(st, ring[s], pw, quad1, grp < nvalid[s], grp + 8 < nvalid[s]);
-      // refill the slot from the group at ci (a re-read when none is left)
-      const int j = ci.j + s < ci.nbr - 1 ? ci.j + s : ci.nbr - 1;
-      const int id = __builtin_amdgcn_readlane(tab, (int)(xr - win) + s);
-      const int nv = issue_block(ring[s], p, id, ci.g, j, ci.ctx, lane_off);
-      nvalid[s] = ci.j + s < ci.nbr ? nv : 0;
+      issue_v(ring[s], p, ub[s], lane_off);
+      nvalid[s] = nv_next[s];
       if (kAppend) {
-        slast[s] = ci.j + s == ci.nbr - 1 && nv > 0;
-        sphys[s] = id;
-      }
-      if (s == 0) {
-        load_q(qn, p, ci.b, ci.g, i, c);
-        if (kAppend) load_new(knn, vnn, p, ci.b, ci.g, i);
+        slast[s] = slast_next[s];
+        sphys[s] = sphys_next[s];
       }
     }
     if (xi + kRing < x1) {
