@@ -212,35 +212,36 @@ prefill_kernel(PParams p) {
     const uint16_t* ks = ks_buf[buf];
     const uint16_t* vt = vt_buf[buf];
 
-    // S^T = K . Q^T  (scores before scaling)
+    // The tile's two 32-column halves (query rows qt*32..qt*32+31) are
+    // independent until the output, so their steps are issued half by half:
+    // the P.V MFMAs of half 0 go out between the VALU work that forms the
+    // weights of half 1, and the two pipes overlap inside one wavefront.
     f32x16 s[2][2];  // [kt][qt]
+    // S^T = K . Q^T for half qt (scores before scaling)
+    auto scores = [&](int qt) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const bf16x8_t a = as_bf16x8(
-            *reinterpret_cast<const u32x4*>(ks + (kt * 32 + lr) * kKRow + 16 * k + 8 * lh));
-        const bf16x8_t q0 = as_bf16x8(qsw[(0 * 4 + k) * 64 + lane]);
-        const bf16x8_t q1 = as_bf16x8(qsw[(1 * 4 + k) * 64 + lane]);
-        s[kt][0] = mfma(a, q0, k == 0 ? kZero16 : s[kt][0]);
-        s[kt][1] = mfma(a, q1, k == 0 ? kZero16 : s[kt][1]);
+        for (int k = 0; k < 4; ++k) {
+          const bf16x8_t a = as_bf16x8(
+              *reinterpret_cast<const u32x4*>(ks + (kt * 32 + lr) * kKRow + 16 * k + 8 * lh));
+          const bf16x8_t qk = as_bf16x8(qsw[(qt * 4 + k) * 64 + lane]);
+          s[kt][qt] = mfma(a, qk, k == 0 ? kZero16 : s[kt][qt]);
+        }
       }
-    }
-
+    };
     // causal mask on tiles that reach past the first row's position: key j of
     // this lane's column is visible iff j <= min(pos, ctx - 1)
-    if (k0 + kTile - 1 > pos_first) {
+    const bool diag = k0 + kTile - 1 > pos_first;
+    auto mask = [&](int qt) {
+      const int pos = pos_first + qt * 32 + lr;
+      const int lim = (pos < ctx - 1 ? pos : ctx - 1) - (k0 + 4 * lh);
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const int pos = pos_first + qt * 32 + lr;
-        const int lim = (pos < ctx - 1 ? pos : ctx - 1) - (k0 + 4 * lh);
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kt][qt][r] = -INFINITY;
-      }
-    }
+        for (int r = 0; r < 16; ++r)
+          if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kt][qt][r] = -INFINITY;
+    };
 
     // Weights against the reference: P^T operand as bf16, and this lane's
     // partial row sums of the same rounded weights (v_dot2 against (1, 1)).
@@ -268,20 +269,15 @@ prefill_kernel(PParams p) {
         }
       lsum[qt] = l0 + l1;
     };
-    weights(0, m_ref[0]);
-    weights(1, m_ref[1]);
 
-    // Exact-max path, wave-uniform and rare: a weight may exceed the bound
-    // (a score rose well above the reference), or a column has no reference
-    // yet.  The reference moves up to the tile max, the accumulator and row
-    // sum are rescaled, and the weights are formed again.  By the softmax
-    // shift identity the result does not depend on the reference used.
-    bool redo = false;
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt) redo = redo || !(lsum[qt] <= kLazyBound) || !has_ref[qt];
-    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
+    // Exact-max path for half qt, wave-uniform and rare: a weight may exceed
+    // the bound (a score rose well above the reference), or a column has no
+    // reference yet.  The reference moves up to the tile max, the accumulator
+    // and row sum are rescaled, and the weights are formed again.  By the
+    // softmax shift identity the result does not depend on the reference used.
+    auto settle = [&](int qt) {
+      const bool redo = !(lsum[qt] <= kLazyBound) || !has_ref[qt];
+      if (__builtin_amdgcn_ballot_w64(redo) != 0) {
         float v = fmaxf(s[0][qt][0], s[0][qt][1]);
 #pragma unroll
         for (int r = 2; r < 16; ++r) v = fmaxf(v, s[0][qt][r]);
@@ -302,24 +298,35 @@ prefill_kernel(PParams p) {
         }
         weights(qt, m_ref[qt]);
       }
-    }
-    l_run[0] += lsum[0];
-    l_run[1] += lsum[1];
+      l_run[qt] += lsum[qt];
+    };
 
-    // O^T += V^T . P^T
+    // O^T += V^T . P^T for half qt
+    auto pv = [&](int qt) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kb = st * 16;  // key offset of this 16-key step within the tile
+      for (int st = 0; st < 4; ++st) {
+        const int kb = st * 16;  // key offset of this 16-key step within the tile
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) {
-        const uint16_t* vrow = vt + (dt * 32 + lr) * kVRow + kb + 4 * lh;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-        const bf16x8_t a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-        o[dt][0] = mfma(a, pop[0][st], o[dt][0]);
-        o[dt][1] = mfma(a, pop[1][st], o[dt][1]);
+        for (int dt = 0; dt < 2; ++dt) {
+          const uint16_t* vrow = vt + (dt * 32 + lr) * kVRow + kb + 4 * lh;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+          const bf16x8_t a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+          o[dt][qt] = mfma(a, pop[qt][st], o[dt][qt]);
+        }
       }
-    }
+    };
+
+    scores(0);
+    if (diag) mask(0);
+    scores(1);
+    weights(0, m_ref[0]);
+    if (diag) mask(1);
+    settle(0);
+    pv(0);
+    weights(1, m_ref[1]);
+    settle(1);
+    pv(1);
 
     store_tile(nxt, ks_buf[buf ^ 1], vt_buf[buf ^ 1], tid);
     __syncthreads();
