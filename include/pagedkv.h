@@ -289,8 +289,9 @@ PKV_API size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int3
  * workspace     device scratch of at least
  *               paged_attention_decode_workspace_size(...) bytes (may be NULL
  *               when that is 0).  It must be zero-filled before its first use;
- *               its first 128 KiB hold per-stream split counters that every
- *               call leaves at zero again, so one zero-fill serves all later
+ *               its first 4 MiB hold per-stream split counters (one per
+ *               128-byte line, so concurrent atomics on different streams
+ *               do not share a line) that every call leaves at zero again, so one zero-fill serves all later
  *               calls, whatever their shapes.  Calls that share a workspace
  *               must not run concurrently (they would race on it).  Splits
  *               handle up to 32768 (sequence, KV head) streams and up to

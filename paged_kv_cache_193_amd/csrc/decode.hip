@@ -426,7 +426,8 @@ __device__ __forceinline__ void drain_stores() {
 __device__ __forceinline__ uint32_t count_piece(const Params& p, int b, int g, int lane) {
   uint32_t before = 0;
   if (lane == 0)
-    before = __hip_atomic_fetch_add(p.ws_count + (int64_t)b * p.Hkv + g, 1u, __ATOMIC_RELAXED,
+    before = __hip_atomic_fetch_add(p.ws_count + ((int64_t)b * p.Hkv + g) * kCounterStride, 1u,
+                                    __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT);
   return __builtin_amdgcn_readfirstlane(before);
 }
@@ -580,7 +581,8 @@ __device__ __forceinline__ void merge_streams(const Params& p, const MergeJob (&
       *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + row) = pk;
     }
     if (lane == 0)
-      __hip_atomic_store(p.ws_count + (int64_t)job[n].b * p.Hkv + job[n].g, 0u, __ATOMIC_RELAXED,
+      __hip_atomic_store(p.ws_count + ((int64_t)job[n].b * p.Hkv + job[n].g) * kCounterStride, 0u,
+                         __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
   }
 }

@@ -65,9 +65,15 @@ constexpr int kRecordFloats = 4 * 64;
 // region at the start of the workspace, whatever the call's shapes, so a
 // workspace zero-filled once stays valid for every later call.
 constexpr int kMaxSplitStreams = 32768;
+// Counters of different streams sit this many uint32 apart, so that
+// concurrent device-scope atomics on different streams do not share a line.
+#ifndef PKV_COUNTER_STRIDE
+#define PKV_COUNTER_STRIDE 32
+#endif
+constexpr int kCounterStride = PKV_COUNTER_STRIDE;
 // Split records addressable with 32-bit byte offsets (1 KB of output each).
 constexpr int kMaxRecords = (1 << 21) - 1;
-constexpr size_t kCounterBytes = (size_t)kMaxSplitStreams * 4;
+constexpr size_t kCounterBytes = (size_t)kMaxSplitStreams * kCounterStride * 4;
 
 // Decode plan (partition PKV_PARTITION_PLANNED), after the split records of
 // the balanced split: a header, the per-sequence prefix of padded block

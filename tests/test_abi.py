@@ -96,7 +96,7 @@ def test_decode_workspace_size(lib):
     assert ws(8, 32, 8, 64, 16, 2048, 0) == 0            # no split
     assert ws(8, 32, 8, 64, 16, 512, 512) == 0           # one partition covers everything
     rec = 4 * 64 + 8                                      # floats per record
-    counters = 32768 * 4                                  # fixed counter region first
+    counters = 32768 * 128                                # fixed counter region first: one per 128 B
     assert ws(4, 32, 8, 64, 16, 32768, 512) == counters + 4 * 8 * 64 * rec * 4
     assert ws(64, 32, 8, 64, 16, 8192, -1) == counters + 2 * 2048 * rec * 4
     assert ws(4097, 32, 8, 64, 16, 8192, 512) == 0        # too many streams -> rejected

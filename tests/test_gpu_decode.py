@@ -14,6 +14,10 @@ import paged_kv_cache_193_amd as pkv
 from paged_kv_cache_193_amd import workloads as wl
 from tests.gpu_util import assert_close, assert_close_bf16, dev, u16
 
+# per-stream split counters at the start of every decode workspace: 32768
+# streams, one uint32 per 128-byte line
+COUNTER_BYTES = 32768 * 128
+
 pytestmark = pytest.mark.gpu
 
 MODES = [pkv.PARTITION_NONE, 32, 512, pkv.PARTITION_AUTO]
@@ -185,7 +189,7 @@ def test_shared_workspace_reused_across_calls(partition):
                                        partition, ws)
             torch.cuda.synchronize()
             assert_close(out.cpu().numpy(), ref, f"reuse p={partition} rep={rep} B={c.B}")
-            counters = ws[:32768 * 4].view(torch.int32)
+            counters = ws[:COUNTER_BYTES].view(torch.int32)
             assert int(counters.abs().sum()) == 0
 
 
@@ -210,4 +214,4 @@ def test_largest_batch_of_the_automatic_split():
         pkv.paged_attention_decode(out, qd, k, v, t, l, 0.125, 40, mode, ws)
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy(), ref, f"B=4096 mode={mode}")
-        assert int(ws[:32768 * 4].view(torch.int32).abs().sum()) == 0   # counters left at zero
+        assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0   # counters left at zero

@@ -13,6 +13,10 @@ import paged_kv_cache_193_amd as pkv
 from paged_kv_cache_193_amd import workloads as wl
 from tests.gpu_util import assert_close, dev, u16
 
+# per-stream split counters at the start of every decode workspace: 32768
+# streams, one uint32 per 128-byte line
+COUNTER_BYTES = 32768 * 128
+
 pytestmark = pytest.mark.gpu
 
 
@@ -86,7 +90,7 @@ def test_plan_reused_across_layers_full_size():
         a = run(c, pkv.PARTITION_AUTO, ws_a, k=k, v=v, lens=lens, tables=tables)
         b = run(c, pkv.PARTITION_PLANNED, ws_p, k=k, v=v, lens=lens, tables=tables)
         assert torch.equal(bits(a), bits(b)), f"layer {layer}"
-        assert int(ws_p[:32768 * 4].view(torch.int32).abs().sum()) == 0
+        assert int(ws_p[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
     del c
     torch.cuda.empty_cache()
 
@@ -142,7 +146,7 @@ def test_stale_plan_is_not_used():
     a3 = run(c3, pkv.PARTITION_AUTO, ws_a3, max_ctx=1024)
     b3 = run(c3, pkv.PARTITION_PLANNED, ws_p, max_ctx=1024)
     assert torch.equal(bits(a3), bits(b3))
-    assert int(ws_p[:32768 * 4].view(torch.int32).abs().sum()) == 0
+    assert int(ws_p[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
 
 
 def test_planned_in_graph():
