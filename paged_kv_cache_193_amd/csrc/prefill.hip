@@ -6,11 +6,15 @@
 // path is a dense contraction, so Q.K^T and P.V run on CDNA4 bf16 MFMA
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
 //
-// Work unit: one workgroup per (64-row query tile, sequence b, KV group g);
+// Work unit: one workgroup per (32-row query tile, sequence b, KV group g);
 // its 4 wavefronts are the 4 query heads of the group, so every K/V tile
 // staged in LDS serves all of them (GQA).  Each wavefront holds, in registers,
-//   S^T[64 keys][64 q]   = K . Q^T       (4 MFMA tiles of 32x32)
-//   O^T[64 d][64 q]     += V^T . P^T     (4 MFMA tiles of 32x32)
+//   S^T[64 keys][32 q]   = K . Q^T       (2 MFMA tiles of 32x32)
+//   O^T[64 d][32 q]     += V^T . P^T     (2 MFMA tiles of 32x32)
+// 32-row query tiles halve the longest unit of work (the last rows of a long
+// prompt see every key tile) and leave room for three workgroups per CU
+// (123 VGPRs, 52 KB of LDS); a one-token row of a mixed batch wastes 31 rows
+// of a tile instead of 63.
 // The MFMA accumulator layout puts one query column and 16 keys in a lane
 // (rows 8*(r/4) + 4*(lane/32) + r%4, column lane%32), which is exactly the
 // layout P^T needs as the B operand of the next product: the softmax runs on
@@ -21,7 +25,7 @@
 // LDS per workgroup, double buffered: K tile [64 keys][64 d] row major and
 // V^T tile [64 d][64 keys] (the B-side key index must run along registers,
 // so V is transposed once per tile here and read back 8 bytes at a time),
-// plus each wavefront's Q^T operand.  Rows are padded to spread LDS banks.
+// plus each wavefront's Q^T operand (32 rows).  Rows are padded to spread LDS banks.
 // Rows of keys past the context, or of an invalid block, are zero filled, so
 // 0 * NaN cannot reach the MFMA.
 //
@@ -51,7 +55,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kD = 64;
 constexpr int kBS = 16;
-constexpr int kTile = 64;          // query rows per workgroup and keys per K/V tile
+constexpr int kTile = 64;          // keys per K/V tile
+constexpr int kQRows = 32;         // query rows per workgroup
 constexpr int kKRow = kD + 8;      // K tile row stride (bf16 elements): 144 bytes
 constexpr int kVRow = kTile + 4;   // V^T tile row stride (bf16 elements): 136 bytes
 // A lane's partial row sum of one tile's weights above this (or not a number)
@@ -134,11 +139,11 @@ __device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* ks, uint
   }
 }
 
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, 3)
 prefill_kernel(PParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t ks_buf[2][kTile * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t vt_buf[2][kD * kVRow];
-  __shared__ u32x4 qs_buf[4][2 * 4 * 64];
+  __shared__ u32x4 qs_buf[4][4 * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -151,13 +156,13 @@ prefill_kernel(PParams p) {
 
   const int qs = p.cu_q_lens[b];
   const int q_len = p.cu_q_lens[b + 1] - qs;
-  const int q0 = tile * kTile;
+  const int q0 = tile * kQRows;
   if (q0 >= q_len) return;
   int ctx = p.context_lens[b];
   const int cap = p.max_blocks * kBS;
   ctx = ctx > cap ? cap : ctx;
   const int hist = ctx - q_len;  // position of query row 0 minus 0
-  const int rows = q_len - q0 < kTile ? q_len - q0 : kTile;
+  const int rows = q_len - q0 < kQRows ? q_len - q0 : kQRows;
   const int pos_first = hist + q0;
   const int pos_last = hist + q0 + rows - 1;
   int kend = pos_last + 1 < ctx ? pos_last + 1 : ctx;  // keys [0, kend)
@@ -166,32 +171,27 @@ prefill_kernel(PParams p) {
   const int h = 4 * g + wave;
   const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks;
 
-  // Q^T operand, kept in LDS: lane holds q row (qt*32 + lane%32), d in
+  // Q^T operand, kept in LDS: lane holds q row q0 + lane%32, d in
   // [k*16 + 8*(lane/32), +8)
   const int lr = lane & 31, lh = lane >> 5;
-  u32x4* qsw = qs_buf[wave];  // this wavefront's Q^T operand [qt][k][lane]
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    int row = q0 + qt * 32 + lr;
+  u32x4* qsw = qs_buf[wave];  // this wavefront's Q^T operand [k][lane]
+  {
+    int row = q0 + lr;
     row = row < q_len ? row : q_len - 1;
     const uint16_t* qr = p.q + ((int64_t)(qs + row) * p.Hq + h) * kD + 8 * lh;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      qsw[(qt * 4 + k) * 64 + lane] = *reinterpret_cast<const u32x4*>(qr + 16 * k) ^
-                                      u32x4{p.q_sign, p.q_sign, p.q_sign, p.q_sign};
+      qsw[k * 64 + lane] = *reinterpret_cast<const u32x4*>(qr + 16 * k) ^
+                           u32x4{p.q_sign, p.q_sign, p.q_sign, p.q_sign};
   }
 
-  f32x16 o[2][2];  // [dt][qt]
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int c = 0; c < 2; ++c) o[a][c] = kZero16;
-  // Reference max m per query column (log2 units): weights are
+  f32x16 o[2] = {kZero16, kZero16};  // [dt]
+  // Reference max m of this lane's query column (log2 units): weights are
   // exp2(c * s - m).  has_ref is false until the column has seen a visible key.
-  float m_ref[2] = {0.f, 0.f};
-  bool has_ref[2] = {false, false};
+  float m_ref = 0.f;
+  bool has_ref = false;
   const float c2 = p.c_log2;
-  float l_run[2] = {0.f, 0.f};  // this lane's share of the row sum
+  float l_run = 0.f;  // this lane's share of the row sum
 
   // K/V tiles go global -> registers -> LDS one tile ahead of the MFMAs, and
   // the block id of the tile after that is read one more tile ahead, so no
@@ -212,42 +212,35 @@ prefill_kernel(PParams p) {
     const uint16_t* ks = ks_buf[buf];
     const uint16_t* vt = vt_buf[buf];
 
-    // The tile's two 32-column halves (query rows qt*32..qt*32+31) are
-    // independent until the output, so their steps are issued half by half:
-    // the P.V MFMAs of half 0 go out between the VALU work that forms the
-    // weights of half 1, and the two pipes overlap inside one wavefront.
-    f32x16 s[2][2];  // [kt][qt]
-    // S^T = K . Q^T for half qt (scores before scaling)
-    auto scores = [&](int qt) {
+    // S^T = K . Q^T (scores before scaling), keys kt*32 .. kt*32+31
+    f32x16 s[2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const bf16x8_t a = as_bf16x8(
-              *reinterpret_cast<const u32x4*>(ks + (kt * 32 + lr) * kKRow + 16 * k + 8 * lh));
-          const bf16x8_t qk = as_bf16x8(qsw[(qt * 4 + k) * 64 + lane]);
-          s[kt][qt] = mfma(a, qk, k == 0 ? kZero16 : s[kt][qt]);
-        }
+      for (int k = 0; k < 4; ++k) {
+        const bf16x8_t a = as_bf16x8(
+            *reinterpret_cast<const u32x4*>(ks + (kt * 32 + lr) * kKRow + 16 * k + 8 * lh));
+        s[kt] = mfma(a, as_bf16x8(qsw[k * 64 + lane]), k == 0 ? kZero16 : s[kt]);
       }
-    };
+    }
+
     // causal mask on tiles that reach past the first row's position: key j of
     // this lane's column is visible iff j <= min(pos, ctx - 1)
-    const bool diag = k0 + kTile - 1 > pos_first;
-    auto mask = [&](int qt) {
-      const int pos = pos_first + qt * 32 + lr;
+    if (k0 + kTile - 1 > pos_first) {
+      const int pos = pos_first + lr;
       const int lim = (pos < ctx - 1 ? pos : ctx - 1) - (k0 + 4 * lh);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kt][qt][r] = -INFINITY;
-    };
+          if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kt][r] = -INFINITY;
+    }
 
     // Weights against the reference: P^T operand as bf16, and this lane's
-    // partial row sums of the same rounded weights (v_dot2 against (1, 1)).
-    bf16x8_t pop[2][4];
-    float lsum[2];
-    auto weights = [&](int qt, float m) {
+    // partial row sum of the same rounded weights (v_dot2 against (1, 1)).
+    bf16x8_t pop[4];
+    float lsum;
+    auto weights = [&](float m) {
       float l0 = 0.f, l1 = 0.f;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -257,105 +250,88 @@ prefill_kernel(PParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 8 * half + 2 * e;
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][r], c2, -m));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][qt][r + 1], c2, -m));
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r], c2, -m));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kt][r + 1], c2, -m));
             w[e] = pack_bf16(p0, p1);
             if (e & 1)
               l1 = dot2_bf16(w[e], kOnesBf16x2, l1);
             else
               l0 = dot2_bf16(w[e], kOnesBf16x2, l0);
           }
-          pop[qt][2 * kt + half] = as_bf16x8(w);
+          pop[2 * kt + half] = as_bf16x8(w);
         }
-      lsum[qt] = l0 + l1;
+      lsum = l0 + l1;
     };
+    weights(m_ref);
 
-    // Exact-max path for half qt, wave-uniform and rare: a weight may exceed
-    // the bound (a score rose well above the reference), or a column has no
-    // reference yet.  The reference moves up to the tile max, the accumulator
-    // and row sum are rescaled, and the weights are formed again.  By the
-    // softmax shift identity the result does not depend on the reference used.
-    auto settle = [&](int qt) {
-      const bool redo = !(lsum[qt] <= kLazyBound) || !has_ref[qt];
-      if (__builtin_amdgcn_ballot_w64(redo) != 0) {
-        float v = fmaxf(s[0][qt][0], s[0][qt][1]);
+    // Exact-max path, wave-uniform and rare: a weight may exceed the bound
+    // (a score rose well above the reference), or a column has no reference
+    // yet.  The reference moves up to the tile max, the accumulator and row
+    // sum are rescaled, and the weights are formed again.  By the softmax
+    // shift identity the result does not depend on the reference used.
+    const bool redo = !(lsum <= kLazyBound) || !has_ref;
+    if (__builtin_amdgcn_ballot_w64(redo) != 0) {
+      float v = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-        for (int r = 2; r < 16; ++r) v = fmaxf(v, s[0][qt][r]);
+      for (int r = 2; r < 16; ++r) v = fmaxf(v, s[0][r]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) v = fmaxf(v, s[1][qt][r]);
-        const float mx = fmaxf(v, shfl_xor(v, 32)) * c2;  // tile max, log2 units
-        // no visible key yet: stay without a reference (weights are 0)
-        if (mx != -INFINITY && mx == mx) {
-          const float m_new = has_ref[qt] ? fmaxf(m_ref[qt], mx) : mx;
-          const float alpha = has_ref[qt] ? __builtin_amdgcn_exp2f(m_ref[qt] - m_new) : 0.f;
-          l_run[qt] *= alpha;
+      for (int r = 0; r < 16; ++r) v = fmaxf(v, s[1][r]);
+      const float mx = fmaxf(v, shfl_xor(v, 32)) * c2;  // tile max, log2 units
+      // no visible key yet: stay without a reference (weights are 0)
+      if (mx != -INFINITY && mx == mx) {
+        const float m_new = has_ref ? fmaxf(m_ref, mx) : mx;
+        const float alpha = has_ref ? __builtin_amdgcn_exp2f(m_ref - m_new) : 0.f;
+        l_run *= alpha;
 #pragma unroll
-          for (int dt = 0; dt < 2; ++dt)
+        for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) o[dt][qt][r] *= alpha;
-          m_ref[qt] = m_new;
-          has_ref[qt] = true;
-        }
-        weights(qt, m_ref[qt]);
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        m_ref = m_new;
+        has_ref = true;
       }
-      l_run[qt] += lsum[qt];
-    };
+      weights(m_ref);
+    }
+    l_run += lsum;
 
-    // O^T += V^T . P^T for half qt
-    auto pv = [&](int qt) {
+    // O^T += V^T . P^T
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const int kb = st * 16;  // key offset of this 16-key step within the tile
+    for (int st = 0; st < 4; ++st) {
+      const int kb = st * 16;  // key offset of this 16-key step within the tile
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const uint16_t* vrow = vt + (dt * 32 + lr) * kVRow + kb + 4 * lh;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-          const bf16x8_t a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-          o[dt][qt] = mfma(a, pop[qt][st], o[dt][qt]);
-        }
+      for (int dt = 0; dt < 2; ++dt) {
+        const uint16_t* vrow = vt + (dt * 32 + lr) * kVRow + kb + 4 * lh;
+        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+        const bf16x8_t a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        o[dt] = mfma(a, pop[st], o[dt]);
       }
-    };
-
-    scores(0);
-    if (diag) mask(0);
-    scores(1);
-    weights(0, m_ref[0]);
-    if (diag) mask(1);
-    settle(0);
-    pv(0);
-    weights(1, m_ref[1]);
-    settle(1);
-    pv(1);
+    }
 
     store_tile(nxt, ks_buf[buf ^ 1], vt_buf[buf ^ 1], tid);
     __syncthreads();
   }
 
   // epilogue: out[row][h][d] = O^T[d][row] / l(row)
+  const float lt = l_run + shfl_xor(l_run, 32);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const int row = q0 + lr;
+  if (row >= q_len) return;
+  const int64_t base = ((int64_t)(qs + row) * p.Hq + h) * kD;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const float lt = l_run[qt] + shfl_xor(l_run[qt], 32);
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    const int row = q0 + qt * 32 + lr;
-    if (row >= q_len) continue;
-    const int64_t base = ((int64_t)(qs + row) * p.Hq + h) * kD;
+  for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int d = dt * 32 + 8 * gq + 4 * lh;
-        const float x0 = o[dt][qt][4 * gq + 0] * inv, x1 = o[dt][qt][4 * gq + 1] * inv;
-        const float x2 = o[dt][qt][4 * gq + 2] * inv, x3 = o[dt][qt][4 * gq + 3] * inv;
-        if (p.out_f32) {
-          *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + base + d) =
-              make_float4(x0, x1, x2, x3);
-        } else {
-          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + base + d) =
-              u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
-        }
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d = dt * 32 + 8 * gq + 4 * lh;
+      const float x0 = o[dt][4 * gq + 0] * inv, x1 = o[dt][4 * gq + 1] * inv;
+      const float x2 = o[dt][4 * gq + 2] * inv, x3 = o[dt][4 * gq + 3] * inv;
+      if (p.out_f32) {
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + base + d) =
+            make_float4(x0, x1, x2, x3);
+      } else {
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + base + d) =
+            u32x2{pack_bf16(x0, x1), pack_bf16(x2, x3)};
       }
-  }
+    }
 }
 
 }  // namespace
@@ -375,7 +351,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.Hkv = a.Hkv;
   p.max_blocks = a.max_blocks_per_seq;
   p.num_blocks = a.num_blocks;
-  p.tiles_max = (a.max_q_len + kTile - 1) / kTile;
+  p.tiles_max = (a.max_q_len + kQRows - 1) / kQRows;
   // |scale| in log2 units, floored so that a zero scale still maps masked
   // (-inf) scores to -inf instead of NaN; any real score times 1e-30 is 0.
   p.c_log2 = (a.scale < 0.f ? -a.scale : a.scale) * kLog2e;
