@@ -26,7 +26,10 @@ prefill workload (4 x 512 + 2 x 2048 prompts) on the bf16 MFMA roofline, and
 6144, on the HBM roofline.  `long_context` times the long-context split
 workload (4 sequences of 32768 tokens) with fixed 512-token partitions merged
 by log-sum-exp, with the balanced split, and with the balanced split's plan
-(made once, outside the timed calls), on the HBM roofline.
+(made once, outside the timed calls), on the HBM roofline.  `mixed_batch`
+times one prefill launch over decode rows and prompt chunks together,
+`copy_blocks` kv_copy_blocks (copy on write), and `scheduler` the host
+block allocator and continuous-batching scheduler per step.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--form planned|auto|two-calls]
 """
@@ -54,6 +57,8 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-rope", action="store_true")
     ap.add_argument("--no-long", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the mixed-batch, block-copy and scheduler legs")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for counter scaling)")
     ap.add_argument("--form", choices=("planned", "auto", "two-calls"), default="planned",
@@ -215,6 +220,167 @@ def run_long_context(torch, pkv, wl, steps, warmup, copies=4):
     del case, k_layers, v_layers
     torch.cuda.empty_cache()
     return res
+
+
+def graph_us(torch, call, steps, warmup, per_graph=8):
+    """Average time of `call` over graph replays (per_graph calls per graph),
+    HIP events on the stream the graph runs on."""
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(per_graph):
+            call()
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(steps):
+        graph.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / (steps * per_graph) * 1e3
+
+
+def run_mixed_batch(torch, pkv, wl, steps, warmup):
+    """One paged_attention_prefill_causal launch over a mixed continuous batch:
+    60 sequences decoding one token each (context log-uniform in [16, 2048])
+    and 4 prompt chunks of 256 tokens on 768 cached tokens (chunked prefill),
+    32q/8kv heads, head_dim 64.  Reported on both rooflines: visible
+    (query, key) pairs x 4 * D * Hq flops against bf16 MFMA peak, and K/V of
+    every context token + q + out + block ids against HBM."""
+    dev = "cuda"
+    g = wl.generator(21)
+    dec_lens = wl.draw_lens(g, 60, ("loguniform", 16, 2048)).tolist()
+    prompts = [1] * 60 + [256] * 4
+    history = [int(L) - 1 for L in dec_lens] + [768] * 4
+    p = wl.prefill_case(seed=21, prompts=prompts, history=history, num_blocks=8192)
+    k, v = p.k_cache.to(dev), p.v_cache.to(dev)
+    t, l, cu = p.block_tables.to(dev), p.context_lens.to(dev), p.cu_q_lens.to(dev)
+    pkv.kv_append(k, v, p.k_new.to(dev), p.v_new.to(dev), t, l, cu)
+    q = p.q.to(dev)
+    out = torch.empty(tuple(p.q.shape), dtype=torch.bfloat16, device=dev)
+    us = graph_us(torch, lambda: pkv.paged_attention_prefill_causal(
+        out, q, k, v, t, l, cu, p.scale, max(prompts)), steps, warmup)
+    # the same batch as two launches: the decode rows through
+    # paged_attention_decode (balanced split), the chunks through the prefill
+    nd = prompts.count(1)
+    out2 = torch.empty_like(out)
+    max_dec = max(h + 1 for h in history[:nd])
+    ws = pkv.decode_workspace(nd, p.Hq, p.Hkv, p.D, 16, max_dec, pkv.PARTITION_AUTO, dev)
+    cu_c = (cu[nd:] - cu[nd]).contiguous()
+
+    def two_launches():
+        pkv.paged_attention_decode(out2[:nd], q[:nd], k, v, t[:nd], l[:nd], p.scale, max_dec,
+                                   pkv.PARTITION_AUTO, ws)
+        pkv.paged_attention_prefill_causal(out2[nd:], q[nd:], k, v, t[nd:], l[nd:], cu_c,
+                                           p.scale, max(prompts[nd:]))
+    us2 = graph_us(torch, two_launches, steps, warmup)
+    # the two launches on two streams (fork and join inside the graph): the
+    # decode rows and the chunks write disjoint rows and only read the pools
+    side = torch.cuda.Stream()
+
+    def two_streams():
+        main = torch.cuda.current_stream()
+        side.wait_stream(main)
+        with torch.cuda.stream(side):
+            pkv.paged_attention_decode(out2[:nd], q[:nd], k, v, t[:nd], l[:nd], p.scale,
+                                       max_dec, pkv.PARTITION_AUTO, ws)
+        pkv.paged_attention_prefill_causal(out2[nd:], q[nd:], k, v, t[nd:], l[nd:], cu_c,
+                                           p.scale, max(prompts[nd:]))
+        main.wait_stream(side)
+    out2.zero_()
+    us3 = graph_us(torch, two_streams, steps, warmup)
+    if not torch.allclose(out.float(), out2.float(), atol=2e-2, rtol=0):
+        raise RuntimeError("mixed batch: the two-stream form differs from the one-launch form")
+    us2_dec = graph_us(torch, lambda: pkv.paged_attention_decode(
+        out2[:nd], q[:nd], k, v, t[:nd], l[:nd], p.scale, max_dec, pkv.PARTITION_AUTO, ws),
+        steps, warmup)
+    us2_pre = graph_us(torch, lambda: pkv.paged_attention_prefill_causal(
+        out2[nd:], q[nd:], k, v, t[nd:], l[nd:], cu_c, p.scale, max(prompts[nd:])), steps, warmup)
+    if not torch.allclose(out.float(), out2.float(), atol=2e-2, rtol=0):
+        raise RuntimeError("mixed batch: the two-launch form differs from the one-launch form")
+    ctx = [h + n for h, n in zip(history, prompts)]
+    pairs = sum(sum(h + i + 1 for i in range(n)) for h, n in zip(history, prompts))
+    flops = pairs * p.Hq * 4 * p.D
+    T = sum(prompts)
+    nbytes = (sum(ctx) * p.Hkv * p.D * 2 * 2 + T * p.Hq * p.D * 2 * 2
+              + sum((c + 15) // 16 for c in ctx) * 4)
+    tflops = flops / (us * 1e-6) / 1e12
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "mixed batch in one prefill launch: 60 decode rows (context "
+                        "log-uniform [16, 2048]) + 4 chunks of 256 tokens on 768 cached "
+                        "tokens, 32q/8kv heads, head_dim 64, bf16",
+            "us_per_call": round(us, 2), "flops": flops, "algorithmic_bytes": nbytes,
+            "roofline_mfma": {"bound": "mfma", "achieved": round(tflops, 1),
+                              "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                              "frac": round(tflops / BF16_PEAK_TFLOPS, 4)},
+            "roofline_hbm": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                             "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)},
+            "two_launches_us": round(us2, 2),
+            "two_streams_us": round(us3, 2),
+            "two_launches_parts_us": {"decode_rows": round(us2_dec, 2),
+                                      "prefill_chunks": round(us2_pre, 2)},
+            "two_launches": "decode rows through paged_attention_decode (balanced split), "
+                            "then the chunks through paged_attention_prefill_causal; "
+                            "two_streams: the same two launches on two streams"}
+
+
+def run_copy_blocks(torch, pkv, wl, steps, warmup):
+    """kv_copy_blocks (copy on write of shared blocks): 64 and 2048 whole
+    blocks (16 KiB of K and 16 KiB of V each, read and written) between
+    disjoint random blocks of an 8192-block pool pair."""
+    dev = "cuda"
+    N, Hkv, bs, D = 8192, wl.HKV, wl.BLOCK_SIZE, wl.HEAD_DIM
+    k = torch.zeros((N, Hkv, bs, D), dtype=torch.bfloat16, device=dev)
+    v = torch.zeros_like(k)
+    perm = torch.randperm(N, generator=wl.generator(41)).to(torch.int32)
+    res = {}
+    for n in (64, 2048):
+        src, dst = perm[:n].to(dev), perm[n:2 * n].to(dev)
+        us = graph_us(torch, lambda: pkv.kv_copy_blocks(k, v, src, dst), steps, warmup)
+        nbytes = n * Hkv * bs * D * 2 * 2 * 2
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[f"blocks_{n}"] = {"us_per_call": round(us, 2), "algorithmic_bytes": nbytes,
+                              "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                           "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+    return res
+
+
+def run_scheduler(pkv, wl, n_requests=512):
+    """Host block allocator + continuous-batching scheduler (pkv_sched_*):
+    512 requests (prompt log-uniform in [16, 2048] tokens, up to 16-512 new
+    tokens), 65536-block pool, batch <= 64, <= 8192 tokens per step, driven
+    to completion; host time per step (C++ plus the ctypes marshalling of
+    the step's arrays) and the share of empty KV slots with paged blocks
+    against static reservations."""
+    g = wl.generator(31)
+    prompt = wl.draw_lens(g, n_requests, ("loguniform", 16, 2048)).tolist()
+    new = wl.draw_lens(g, n_requests, ("loguniform", 16, 512)).tolist()
+    s = pkv.Scheduler(65536, wl.BLOCK_SIZE, 512, 64, 8192)
+    for rid in range(n_requests):
+        s.add_request(rid, int(prompt[rid]), int(new[rid]))
+    n_steps = 0
+    t0 = time.perf_counter()
+    while n_steps < 100000:
+        b = s.step()
+        if len(b["seq_ids"]) == 0:
+            break
+        n_steps += 1
+    secs = time.perf_counter() - t0
+    st = s.stats()
+    s.close()
+    cached = st["cached_token_steps"]
+    return {"workload": "512 requests, prompt log-uniform [16, 2048], new tokens log-uniform "
+                        "[16, 512], 65536-block pool, batch <= 64, <= 8192 tokens per step",
+            "steps": n_steps, "us_per_step": round(secs / max(n_steps, 1) * 1e6, 2),
+            "finished": st["finished"], "preemptions": st["preemptions"],
+            "empty_slot_share": {
+                "paged": round(1 - cached / st["paged_slot_steps"], 4),
+                "static_per_request_max": round(1 - cached / st["static_request_slot_steps"], 4),
+                "static_max_length": round(1 - cached / st["static_max_slot_steps"], 4)}}
 
 
 def rope_append_bytes(T, Hq, Hkv, D):
@@ -440,6 +606,17 @@ def main():
                                                       args.warmup)
         except pkv.PagedKVError as e:
             result["long_context"] = {"error": str(e)}
+
+    if not args.no_next:
+        for key, fn in (("mixed_batch", lambda: run_mixed_batch(torch, pkv, wl, max(args.steps, 10),
+                                                                args.warmup)),
+                        ("copy_blocks", lambda: run_copy_blocks(torch, pkv, wl, max(args.steps, 10),
+                                                                args.warmup)),
+                        ("scheduler", lambda: run_scheduler(pkv, wl))):
+            try:
+                result[key] = fn()
+            except pkv.PagedKVError as e:
+                result[key] = {"error": str(e)}
 
     if not args.no_rope:
         try:
