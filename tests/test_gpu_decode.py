@@ -169,6 +169,18 @@ def test_long_context_split_full_size():
     assert_close(got.cpu().numpy(), ref, "long 512")
     auto = gpu_decode(c, pkv.PARTITION_AUTO, k=c.extra["k_layers"][0], v=c.extra["v_layers"][0])
     assert_close(auto.cpu().numpy(), ref, "long auto")
+    # with the balanced split's plan (as the benchmark times it): the same bits
+    k, v = c.extra["k_layers"][0], c.extra["v_layers"][0]
+    t, l = dev(c.block_tables), dev(c.context_lens)
+    ws = pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, c.block_size, c.max_context_len,
+                              pkv.PARTITION_PLANNED, "cuda")
+    pkv.paged_attention_decode_plan(k, t, l, c.Hq, c.max_context_len, ws)
+    planned = torch.full_like(auto, float("nan"))
+    pkv.paged_attention_decode(planned, dev(c.q), k, v, t, l, c.scale, c.max_context_len,
+                               pkv.PARTITION_PLANNED, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(planned, auto), "planned long-context call differs from the automatic split"
+    assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
     del c
     torch.cuda.empty_cache()
 
