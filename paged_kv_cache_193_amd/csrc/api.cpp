@@ -371,6 +371,9 @@ int paged_attention_prefill_causal(void* out, int32_t out_dtype, const void* q,
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_ERR_INVALID_ARG, "out, q and the pools must be 16-byte aligned");
+  if (pkv::prefill_grid_size(max_q_len, T_q, B, Hkv) > INT32_MAX)
+    return fail(PKV_ERR_UNSUPPORTED, "%lld workgroups exceed one launch's grid",
+                (long long)pkv::prefill_grid_size(max_q_len, T_q, B, Hkv));
   pkv::PrefillArgs a;
   a.out = out;
   a.out_f32 = out_dtype == PKV_OUT_F32;

@@ -129,5 +129,8 @@ struct PrefillArgs {
   float scale;
 };
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// Workgroups launch_prefill would start for these arguments (one per
+// 32-row query tile of the longest prompt, sequence and KV head).
+int64_t prefill_grid_size(int32_t max_q_len, int32_t T_q, int32_t B, int32_t Hkv);
 
 }  // namespace pkv

@@ -336,6 +336,12 @@ prefill_kernel(PParams p) {
 
 }  // namespace
 
+int64_t prefill_grid_size(int32_t max_q_len, int32_t T_q, int32_t B, int32_t Hkv) {
+  // no prompt is longer than all the query tokens together
+  const int64_t rows = max_q_len < T_q ? max_q_len : T_q;
+  return (rows + kQRows - 1) / kQRows * B * Hkv;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   PParams p;
   p.out = a.out;
@@ -351,13 +357,14 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.Hkv = a.Hkv;
   p.max_blocks = a.max_blocks_per_seq;
   p.num_blocks = a.num_blocks;
-  p.tiles_max = (a.max_q_len + kQRows - 1) / kQRows;
+  const int32_t rows = a.max_q_len < a.T_q ? a.max_q_len : a.T_q;
+  p.tiles_max = (rows + kQRows - 1) / kQRows;
   // |scale| in log2 units, floored so that a zero scale still maps masked
   // (-inf) scores to -inf instead of NaN; any real score times 1e-30 is 0.
   p.c_log2 = (a.scale < 0.f ? -a.scale : a.scale) * kLog2e;
   if (p.c_log2 < 1e-30f) p.c_log2 = 1e-30f;
   p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
-  const int64_t grid = (int64_t)p.tiles_max * a.B * a.Hkv;
+  const int64_t grid = prefill_grid_size(a.max_q_len, a.T_q, a.B, a.Hkv);
   hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -274,6 +274,8 @@ def prefill_call(lib, **kw):
     (dict(maxq=-1), pkv.PKV_ERR_INVALID_ARG),
     (dict(out_dtype=3), pkv.PKV_ERR_INVALID_ARG),
     (dict(scale=float("nan")), pkv.PKV_ERR_INVALID_ARG),
+    # 2^31 - 1 query tokens over 2^20 sequences: more workgroups than one grid
+    (dict(B=1 << 20, T=2 ** 31 - 1, maxq=2 ** 31 - 1), pkv.PKV_ERR_UNSUPPORTED),
 ])
 def test_prefill_rejects(lib, kw, code):
     assert prefill_call(lib, **kw) == code
