@@ -22,10 +22,11 @@
 // statistics (max, sum) are per query column: in-lane over 32 keys plus one
 // exchange with lane^32.
 //
-// LDS per workgroup, double buffered: K tile [64 keys][64 d] row major and
-// V^T tile [64 d][64 keys] (the B-side key index must run along registers,
-// so V is transposed once per tile here and read back 8 bytes at a time),
-// plus each wavefront's Q^T operand (32 rows).  Rows are padded to spread LDS banks.
+// LDS per workgroup, double buffered: K and V tiles [64 keys][64 d], both
+// row major, plus each wavefront's Q^T operand (32 rows).  The V^T operand
+// of P.V needs consecutive keys of one head_dim column in a lane; CDNA4's
+// transposing LDS read (ds_read_b64_tr_b16) delivers them straight from the
+// row-major tile, so V is not transposed at staging.  Rows are padded to spread LDS banks.
 // Rows of keys past the context, or of an invalid block, are zero filled, so
 // 0 * NaN cannot reach the MFMA.
 //
@@ -57,8 +58,7 @@ constexpr int kD = 64;
 constexpr int kBS = 16;
 constexpr int kTile = 64;          // keys per K/V tile
 constexpr int kQRows = 32;         // query rows per workgroup
-constexpr int kKRow = kD + 8;      // K tile row stride (bf16 elements): 144 bytes
-constexpr int kVRow = kTile + 4;   // V^T tile row stride (bf16 elements): 136 bytes
+constexpr int kKRow = kD + 8;      // K and V tile row stride (bf16 elements): 144 bytes
 // A lane's partial row sum of one tile's weights above this (or not a number)
 // sends the tile through the exact-max path.  Weights stay below 2^10.
 constexpr float kLazyBound = 1024.f;
@@ -124,25 +124,34 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const PParams& p, int phy
   if (!(ok && key0 + 1 < ctx)) r.k1 = r.v1 = zero;
 }
 
-__device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* ks, uint16_t* vt,
+__device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* ks, uint16_t* vs,
                                            int tid) {
   const int kp = tid >> 3, c = tid & 7;
   *reinterpret_cast<u32x4*>(ks + (2 * kp) * kKRow + 8 * c) = r.k0;
   *reinterpret_cast<u32x4*>(ks + (2 * kp + 1) * kKRow + 8 * c) = r.k1;
-  // V^T[d][key]: pair keys (2kp, 2kp+1) at each d into one dword
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t lo = __builtin_amdgcn_perm(r.v1[w], r.v0[w], 0x05040100u);  // d = 8c+2w
-    const uint32_t hi = __builtin_amdgcn_perm(r.v1[w], r.v0[w], 0x07060302u);  // d = 8c+2w+1
-    *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * w) * kVRow + 2 * kp) = lo;
-    *reinterpret_cast<uint32_t*>(vt + (8 * c + 2 * w + 1) * kVRow + 2 * kp) = hi;
-  }
+  // V row major like K; the P.V operand reads it transposed (ds_read_b64_tr_b16)
+  *reinterpret_cast<u32x4*>(vs + (2 * kp) * kKRow + 8 * c) = r.v0;
+  *reinterpret_cast<u32x4*>(vs + (2 * kp + 1) * kKRow + 8 * c) = r.v1;
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// Four consecutive keys at one head_dim column, transposed out of the
+// row-major V tile: in each group of 16 lanes, lane 4k+p addresses row
+// key0+k at columns d0+4p..d0+4p+3, and lane i receives rows key0..key0+3
+// of column d0+i.
+__device__ __forceinline__ u32x2 v_keys4(const uint16_t* vs, int key0, int d0, int lane) {
+  const int j = lane & 15;
+  const uint16_t* a = vs + (key0 + (j >> 2)) * kKRow + d0 + 4 * (j & 3);
+  const v4i16 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4i16*)(a));
+  return __builtin_bit_cast(u32x2, x);
 }
 
 __global__ void __launch_bounds__(256, 3)
 prefill_kernel(PParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t ks_buf[2][kTile * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_buf[2][kD * kVRow];
+  __shared__ __attribute__((aligned(16))) uint16_t vs_buf[2][kTile * kKRow];
   __shared__ u32x4 qs_buf[4][4 * 64];
 
   const int tid = threadIdx.x;
@@ -199,7 +208,7 @@ prefill_kernel(PParams p) {
   TileRegs nxt;
   int id_next = tile_block_id(p, trow, kTile, tid);
   load_tile(nxt, p, tile_block_id(p, trow, 0, tid), g, ctx, 0, tid);
-  store_tile(nxt, ks_buf[0], vt_buf[0], tid);
+  store_tile(nxt, ks_buf[0], vs_buf[0], tid);
   __syncthreads();
 
   for (int it = 0; it < n_tiles; ++it) {
@@ -210,7 +219,7 @@ prefill_kernel(PParams p) {
     load_tile(nxt, p, id_next, g, ctx, k0 + kTile, tid);
     id_next = tile_block_id(p, trow, k0 + 2 * kTile, tid);
     const uint16_t* ks = ks_buf[buf];
-    const uint16_t* vt = vt_buf[buf];
+    const uint16_t* vs = vs_buf[buf];
 
     // S^T = K . Q^T (scores before scaling), keys kt*32 .. kt*32+31
     f32x16 s[2];
@@ -299,15 +308,16 @@ prefill_kernel(PParams p) {
       const int kb = st * 16;  // key offset of this 16-key step within the tile
 #pragma unroll
       for (int dt = 0; dt < 2; ++dt) {
-        const uint16_t* vrow = vt + (dt * 32 + lr) * kVRow + kb + 4 * lh;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+        // column dt*32 + lr: the group of 16 lanes starts at dt*32 + 16*(lane/16 % 2)
+        const int d0 = dt * 32 + (lr & 16);
+        const u32x2 lo = v_keys4(vs, kb + 4 * lh, d0, lane);
+        const u32x2 hi = v_keys4(vs, kb + 8 + 4 * lh, d0, lane);
         const bf16x8_t a = as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
         o[dt] = mfma(a, pop[st], o[dt]);
       }
     }
 
-    store_tile(nxt, ks_buf[buf ^ 1], vt_buf[buf ^ 1], tid);
+    store_tile(nxt, ks_buf[buf ^ 1], vs_buf[buf ^ 1], tid);
     __syncthreads();
   }
 
