@@ -13,7 +13,7 @@
 //   O^T[64 d][32 q]     += V^T . P^T     (2 MFMA tiles of 32x32)
 // 32-row query tiles halve the longest unit of work (the last rows of a long
 // prompt see every key tile) and leave room for three workgroups per CU
-// (123 VGPRs, 52 KB of LDS); a one-token row of a mixed batch wastes 31 rows
+// (135 VGPRs, 36 KB of LDS); a one-token row of a mixed batch wastes 31 rows
 // of a tile instead of 63.
 // The MFMA accumulator layout puts one query column and 16 keys in a lane
 // (rows 8*(r/4) + 4*(lane/32) + r%4, column lane%32), which is exactly the
@@ -23,7 +23,8 @@
 // exchange with lane^32.
 //
 // LDS per workgroup, double buffered: K and V tiles [64 keys][64 d], both
-// row major, plus each wavefront's Q^T operand (32 rows).  The V^T operand
+// row major (36 KB); each wavefront keeps its Q^T operand (32 rows, 16
+// VGPRs) in registers.  The V^T operand
 // of P.V needs consecutive keys of one head_dim column in a lane; CDNA4's
 // transposing LDS read (ds_read_b64_tr_b16) delivers them straight from the
 // row-major tile, so V is not transposed at staging.  Rows are padded to spread LDS banks.
@@ -152,7 +153,6 @@ __global__ void __launch_bounds__(256, 3)
 prefill_kernel(PParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t ks_buf[2][kTile * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t vs_buf[2][kTile * kKRow];
-  __shared__ u32x4 qs_buf[4][4 * 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -180,17 +180,17 @@ prefill_kernel(PParams p) {
   const int h = 4 * g + wave;
   const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks;
 
-  // Q^T operand, kept in LDS: lane holds q row q0 + lane%32, d in
+  // Q^T operand, in registers: lane holds q row q0 + lane%32, d in
   // [k*16 + 8*(lane/32), +8)
   const int lr = lane & 31, lh = lane >> 5;
-  u32x4* qsw = qs_buf[wave];  // this wavefront's Q^T operand [k][lane]
+  u32x4 qsw[4];  // this wavefront's Q^T operand [k], in registers
   {
     int row = q0 + lr;
     row = row < q_len ? row : q_len - 1;
     const uint16_t* qr = p.q + ((int64_t)(qs + row) * p.Hq + h) * kD + 8 * lh;
 #pragma unroll
     for (int k = 0; k < 4; ++k)
-      qsw[k * 64 + lane] = *reinterpret_cast<const u32x4*>(qr + 16 * k) ^
+      qsw[k] = *reinterpret_cast<const u32x4*>(qr + 16 * k) ^
                            u32x4{p.q_sign, p.q_sign, p.q_sign, p.q_sign};
   }
 
@@ -229,7 +229,7 @@ prefill_kernel(PParams p) {
       for (int k = 0; k < 4; ++k) {
         const bf16x8_t a = as_bf16x8(
             *reinterpret_cast<const u32x4*>(ks + (kt * 32 + lr) * kKRow + 16 * k + 8 * lh));
-        s[kt] = mfma(a, as_bf16x8(qsw[k * 64 + lane]), k == 0 ? kZero16 : s[kt]);
+        s[kt] = mfma(a, as_bf16x8(qsw[k]), k == 0 ? kZero16 : s[kt]);
       }
     }
 
