@@ -23,13 +23,13 @@
 // exchange with lane^32.
 //
 // LDS per workgroup, double buffered: K and V tiles [64 keys][64 d], both
-// row major (36 KB); each wavefront keeps its Q^T operand (32 rows, 16
-// VGPRs) in registers.  The V^T operand
+// row major with rows padded to spread LDS banks (36 KB); each wavefront
+// keeps its Q^T operand (32 rows, 16 VGPRs) in registers.  The V^T operand
 // of P.V needs consecutive keys of one head_dim column in a lane; CDNA4's
 // transposing LDS read (ds_read_b64_tr_b16) delivers them straight from the
-// row-major tile, so V is not transposed at staging.  Rows are padded to spread LDS banks.
-// Rows of keys past the context, or of an invalid block, are zero filled, so
-// 0 * NaN cannot reach the MFMA.
+// row-major tile, so V is not transposed at staging.  Rows of keys past the
+// context, or of an invalid block, are zero filled, so 0 * NaN cannot reach
+// the MFMA.
 //
 // Softmax (fp32, log2 units): weights are exp2(c * s - m) against a reference
 // maximum m per query column.  m is not recomputed every tile: only when a
