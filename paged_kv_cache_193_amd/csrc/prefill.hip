@@ -248,7 +248,7 @@ prefill_kernel(PParams p) {
     // Weights against the reference: P^T operand as bf16, and this lane's
     // partial row sum of the same rounded weights (v_dot2 against (1, 1)).
     bf16x8_t pop[4];
-    float lsum;
+    float lsum = 0.f;
     auto weights = [&](float m) {
       float l0 = 0.f, l1 = 0.f;
 #pragma unroll
@@ -271,14 +271,18 @@ prefill_kernel(PParams p) {
         }
       lsum = l0 + l1;
     };
-    weights(m_ref);
+    // The first tile goes straight to the exact path (no column has a
+    // reference yet; every column sees key 0, so each gets one there).
+    const bool first = it == 0;
+    if (!first) weights(m_ref);
 
-    // Exact-max path, wave-uniform and rare: a weight may exceed the bound
-    // (a score rose well above the reference), or a column has no reference
-    // yet.  The reference moves up to the tile max, the accumulator and row
-    // sum are rescaled, and the weights are formed again.  By the softmax
-    // shift identity the result does not depend on the reference used.
-    const bool redo = !(lsum <= kLazyBound) || !has_ref;
+    // Exact-max path, wave-uniform and rare after the first tile: a weight
+    // may exceed the bound (a score rose well above the reference), or a
+    // column has no reference yet.  The reference moves up to the tile max,
+    // the accumulator and row sum are rescaled, and the weights are formed
+    // again.  By the softmax shift identity the result does not depend on the
+    // reference used.
+    const bool redo = first || !(lsum <= kLazyBound) || !has_ref;
     if (__builtin_amdgcn_ballot_w64(redo) != 0) {
       float v = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
