@@ -36,8 +36,8 @@
  *   - Table entries past ceil(context_lens[b] / block_size) and pool rows past
  *     the context are never read.  Physical ids outside [0, num_blocks) and
  *     contexts longer than max_blocks_per_seq * block_size are data errors:
- *     the kernels never touch memory outside the pools for them (such blocks
- *     are skipped) but the result for that sequence is then undefined.
+ *     the kernels never touch memory outside the pools for them, but the
+ *     result for that sequence is then undefined.
  *   - Return: PKV_OK, or a negative status; pagedkv_last_error() gives text.
  *     Validation happens on the host before any HIP call, so invalid
  *     arguments never reach the device.  B == 0 (or no new tokens) returns

@@ -28,8 +28,8 @@
 // of P.V needs consecutive keys of one head_dim column in a lane; CDNA4's
 // transposing LDS read (ds_read_b64_tr_b16) delivers them straight from the
 // row-major tile, so V is not transposed at staging.  Rows of keys past the
-// context, or of an invalid block, are zero filled, so 0 * NaN cannot reach
-// the MFMA.
+// context (only the tile that reaches past it has any) are zero filled, so
+// 0 * NaN cannot reach the MFMA; an invalid block id reads block 0 instead.
 //
 // Softmax (fp32, log2 units): weights are exp2(c * s - m) against a reference
 // maximum m per query column.  m is not recomputed every tile: only when a
@@ -120,9 +120,14 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const PParams& p, int phy
   r.v0 = *reinterpret_cast<const u32x4*>(p.v_cache + base);
   r.k1 = *reinterpret_cast<const u32x4*>(p.k_cache + base + kD);
   r.v1 = *reinterpret_cast<const u32x4*>(p.v_cache + base + kD);
-  const u32x4 zero = {0, 0, 0, 0};
-  if (!(ok && key0 < ctx)) r.k0 = r.v0 = zero;
-  if (!(ok && key0 + 1 < ctx)) r.k1 = r.v1 = zero;
+  // Only a tile that reaches past the context holds rows to zero (a wave-
+  // uniform test); inside the context the table's ids are valid by contract
+  // (an invalid one reads block 0, in bounds, and gives an undefined result).
+  if (k0 + kTile > ctx) {
+    const u32x4 zero = {0, 0, 0, 0};
+    if (!(ok && key0 < ctx)) r.k0 = r.v0 = zero;
+    if (!(ok && key0 + 1 < ctx)) r.k1 = r.v1 = zero;
+  }
 }
 
 __device__ __forceinline__ void store_tile(const TileRegs& r, uint16_t* ks, uint16_t* vs,
