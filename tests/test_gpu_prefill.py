@@ -134,3 +134,25 @@ def test_long_prompt_sampled_rows():
     ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
                                 p.cu_q_lens.numpy(), p.scale, rows=rows)
     assert_close(out.cpu().numpy()[rows], ref[rows], "8192-token prompt, sampled rows")
+
+
+@pytest.mark.parametrize("slope", [0.15, 0.6, -0.15, -0.6])
+def test_monotone_scores(slope):
+    """Scores that rise along the keys (by `slope` natural-log units per key)
+    move each row's softmax reference on every 64-key tile; scores that fall
+    leave the first key dominant and make every later weight underflow.  Both
+    extremes of the online softmax must still match the oracle."""
+    p = wl.prefill_case(prompts=[300, 130, 1], num_blocks=64, seed=73, poison=True)
+    D = p.q.shape[-1]
+    p.q.fill_(0.25)
+    cu = p.cu_q_lens.tolist()
+    for b in range(len(cu) - 1):
+        j = torch.arange(cu[b + 1] - cu[b], dtype=torch.float32)
+        # score(i, j) = scale * sum_d q_d k_jd = slope * j
+        kval = slope * j / (p.scale * D * 0.25)
+        p.k_new[cu[b]:cu[b + 1]] = kval[:, None, None].to(torch.bfloat16)
+    k, v, kr, vr = appended(p)
+    ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
+                                p.cu_q_lens.numpy(), p.scale)
+    got = gpu_prefill(p, k, v)
+    assert_close(got.cpu().numpy(), ref, f"prefill monotone slope {slope}")
