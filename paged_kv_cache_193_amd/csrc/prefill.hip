@@ -162,20 +162,25 @@ prefill_kernel(PParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // grid: g fastest, then b, then query tile from the last (heaviest) down
+  // grid: g fastest, then b, then a rank per query tile.  A prompt without
+  // cached history takes its tiles from the last (heaviest) down.  With
+  // history, tile 0 already sees the whole history and can be the heaviest
+  // unit of the launch (a decode row of a mixed batch is only tile 0), so
+  // it takes the first rank and the other tiles follow from the last down.
   const int g = blockIdx.x % p.Hkv;
   const int rest = blockIdx.x / p.Hkv;
   const int b = rest % p.B;
-  const int tile = p.tiles_max - 1 - rest / p.B;
+  const int rank = rest / p.B;
 
   const int qs = p.cu_q_lens[b];
   const int q_len = p.cu_q_lens[b + 1] - qs;
-  const int q0 = tile * kQRows;
-  if (q0 >= q_len) return;
   int ctx = p.context_lens[b];
   const int cap = p.max_blocks * kBS;
   ctx = ctx > cap ? cap : ctx;
   const int hist = ctx - q_len;  // position of query row 0 minus 0
+  const int tile = hist <= 0 ? p.tiles_max - 1 - rank : rank == 0 ? 0 : p.tiles_max - rank;
+  const int q0 = tile * kQRows;
+  if (q0 >= q_len) return;
   const int rows = q_len - q0 < kQRows ? q_len - q0 : kQRows;
   const int pos_first = hist + q0;
   const int pos_last = hist + q0 + rows - 1;
