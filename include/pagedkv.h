@@ -381,7 +381,9 @@ PKV_API int paged_attention_decode_append(void *out, int32_t out_dtype, const vo
  * q             [T_q][Hq][D] bf16, packed by sequence.
  * cu_q_lens     [B+1] int32 prefix sums of query tokens per sequence.
  * max_q_len     host-side upper bound of the per-sequence query counts
- *               (values above T_q are taken as T_q).
+ *               (values above T_q are taken as T_q).  Query tiles are
+ *               launched for the first max_q_len rows of each sequence
+ *               only: rows past them in a longer sequence are not written.
  * Other arguments as for decode.  This build implements D == 64,
  * block_size == 16 and Hq == 4 * Hkv.  One workgroup runs per 32-row query
  * tile of max_q_len, sequence and KV head; more than 2^31 - 1 of them return

@@ -156,3 +156,25 @@ def test_monotone_scores(slope):
                                 p.cu_q_lens.numpy(), p.scale)
     got = gpu_prefill(p, k, v)
     assert_close(got.cpu().numpy(), ref, f"prefill monotone slope {slope}")
+
+
+@pytest.mark.parametrize("history", [None, [50, 0]])
+def test_rows_past_max_q_len_untouched(history):
+    """max_q_len below a sequence's query count: the first max_q_len rows of
+    every sequence are computed (whichever order its tiles are dispatched in)
+    and the rows past them keep what the output held."""
+    p = wl.prefill_case(prompts=[100, 40], history=history, num_blocks=64, seed=74, poison=True)
+    k, v, kr, vr = appended(p)
+    ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
+                                p.cu_q_lens.numpy(), p.scale)
+    out = torch.full(tuple(p.q.shape), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_attention_prefill_causal(out, dev(p.q), k, v, dev(p.block_tables),
+                                       dev(p.context_lens), dev(p.cu_q_lens), p.scale, 64)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    cu = p.cu_q_lens.tolist()
+    done = np.zeros(got.shape[0], dtype=bool)
+    for b in range(len(cu) - 1):
+        done[cu[b]:min(cu[b + 1], cu[b] + 64)] = True
+    assert_close(got[done], ref[done], f"prefill max_q_len 64 hist {history}")
+    assert np.isnan(got[~done]).all()
