@@ -43,8 +43,10 @@
 // context_len tokens sits at position context_len - q_len + t and sees keys
 // 0..pos.  Key tiles entirely below the first row's position need no mask;
 // only diagonal tiles are masked.  Query tiles are launched heaviest first
-// and the KV group is the fastest-varying grid index (one KV head per XCD's
-// L2 for the 8-head case).
+// as far as the grid index can tell (a prompt's last tile first; tile 0
+// first where cached history makes it the heavy one), and the KV group is
+// the fastest-varying grid index (one KV head per XCD's L2 for the 8-head
+// case).
 #include "device_common.h"
 #include "launch.h"
 
