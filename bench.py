@@ -69,6 +69,9 @@ def parse():
                          "without a plan; two-calls: kv_append then paged_attention_decode")
     ap.add_argument("--partition", type=int, default=-1,
                     help="decode partition_size (-1 = automatic balanced split)")
+    ap.add_argument("--only", choices=("prefill", "long", "mixed"), default=None,
+                    help="run this one leg alone and print its JSON object (for profiling "
+                         "a single kernel); the contract line is not printed")
     return ap.parse_args()
 
 
@@ -208,7 +211,7 @@ def run_long_context(torch, pkv, wl, steps, warmup, copies=4):
            "algorithmic_bytes": dec_b}
     for name, part in (("partition_512", 512), ("auto", pkv.PARTITION_AUTO),
                        ("planned", pkv.PARTITION_PLANNED)):
-        ws = pkv.decode_workspace(B, Hq, Hkv, D, 16, max_ctx, part, dev)
+        ws = pkv.decode_workspace(B, Hq, D, max_ctx, part, dev)
         if part == pkv.PARTITION_PLANNED:  # lengths and tables stay fixed: plan once
             pkv.paged_attention_decode_plan(k_layers[0], t, l, Hq, max_ctx, ws)
 
@@ -252,7 +255,7 @@ def run_mixed_batch(torch, pkv, wl, steps, warmup):
     nd = prompts.count(1)
     out2 = torch.empty_like(out)
     max_dec = max(h + 1 for h in history[:nd])
-    ws = pkv.decode_workspace(nd, p.Hq, p.Hkv, p.D, 16, max_dec, pkv.PARTITION_AUTO, dev)
+    ws = pkv.decode_workspace(nd, p.Hq, p.D, max_dec, pkv.PARTITION_AUTO, dev)
     cu_c = (cu[nd:] - cu[nd]).contiguous()
 
     def two_launches():
@@ -417,6 +420,12 @@ def main():
 
     pkv.load_library()
     dev = "cuda"
+    if args.only is not None:
+        steps = max(args.steps, 10)
+        fn = {"prefill": run_prefill, "long": run_long_context, "mixed": run_mixed_batch}[args.only]
+        print(json.dumps({"only": args.only, args.only: fn(torch, pkv, wl, steps, args.warmup)}),
+              flush=True)
+        return
     case = wl.device_decode_case("ragged", dev, layers=LAYERS)
     k_layers, v_layers = case.extra["k_layers"], case.extra["v_layers"]
     B, Hq, Hkv, D = case.B, case.Hq, case.Hkv, case.D
@@ -424,8 +433,8 @@ def main():
     k_new, v_new = case.k_new.to(dev), case.v_new.to(dev)
     max_ctx = case.max_context_len
     outs = [torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(LAYERS)]
-    ws = pkv.decode_workspace(B, Hq, Hkv, D, 16, max_ctx, args.partition, dev)
-    ws_plan = pkv.decode_workspace(B, Hq, Hkv, D, 16, max_ctx, pkv.PARTITION_PLANNED, dev)
+    ws = pkv.decode_workspace(B, Hq, D, max_ctx, args.partition, dev)
+    ws_plan = pkv.decode_workspace(B, Hq, D, max_ctx, pkv.PARTITION_PLANNED, dev)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20

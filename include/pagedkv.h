@@ -74,7 +74,16 @@ extern "C" {
 #define PKV_PARTITION_AUTO (-1) /* balanced split of all blocks over the GPU  */
 #define PKV_PARTITION_PLANNED (-2) /* PKV_PARTITION_AUTO from a stored plan      */
 
-/* Text describing the last non-OK status returned on the calling thread. */
+/* pagedkv_last_error -- text describing the last non-OK status returned on
+ * the calling thread (thread-local; "" before any failure).
+ *
+ * Defined by: paper-digest page, section "Evidence" -- the community's
+ * criticism that the CUDA engine ignores the status codes its runtime calls
+ * return, which makes failures hard to debug.  Here every entry point
+ * returns a status (PKV_OK or a negative PKV_ERR_*), HIP errors included,
+ * and leaves the reason in this string.  The pointer stays valid until the
+ * next failing call on the same thread; the caller must not free it.
+ */
 PKV_API const char *pagedkv_last_error(void);
 
 /* kv_append -- store the new tokens' K and V rows into the paged pools.
@@ -250,11 +259,24 @@ PKV_API int32_t pkv_sched_events(const pkv_scheduler *s, int32_t which, int64_t 
 /* Counters (PKV_SCHED_STATS int64 values, see above) into out. */
 PKV_API int pkv_sched_stats(const pkv_scheduler *s, int64_t *out);
 
-/* Bytes of device workspace paged_attention_decode needs for these arguments
- * (0 when no split is requested).  Pure function of its arguments; makes no
- * HIP call.  Returns 0 for arguments decode would reject. */
-PKV_API size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv,
-                                             int32_t D, int32_t block_size,
+/* paged_attention_decode_workspace_size -- bytes of device workspace that
+ * paged_attention_decode (and _decode_append, _decode_plan) needs for these
+ * arguments, 0 when the call splits nothing.
+ *
+ * Defined by: the split-context form of decode attention -- partial results
+ * (o_p, m_p, l_p) of a sequence's key ranges kept until they are merged by
+ * log-sum-exp, the online-softmax identity of README table of contents
+ * "Online softmax" applied to partitions.  The pages give no interface; the
+ * caller owns and sizes every device buffer (the library allocates nothing),
+ * so the size of the scratch the split needs is a query.
+ *
+ * B, Hq, D, max_context_len, partition_size as for paged_attention_decode.
+ * This build implements one GQA group (Hq == 4 * Hkv) and one block size
+ * (16), so the KV head count is Hq / 4 and the block size 16.  Pure function
+ * of its arguments; makes no HIP call.  Returns 0 (and sets
+ * pagedkv_last_error) for arguments decode would reject.
+ */
+PKV_API size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int32_t D,
                                              int32_t max_context_len,
                                              int32_t partition_size);
 
@@ -385,9 +407,9 @@ PKV_API int paged_attention_decode_append(void *out, int32_t out_dtype, const vo
  *               launched for the first max_q_len rows of each sequence
  *               only: rows past them in a longer sequence are not written.
  * Other arguments as for decode.  This build implements D == 64,
- * block_size == 16 and Hq == 4 * Hkv.  One workgroup runs per 32-row query
- * tile of max_q_len, sequence and KV head; more than 2^31 - 1 of them return
- * PKV_ERR_UNSUPPORTED.
+ * block_size == 16 and Hq == 4 * Hkv.  One workgroup of 256 threads runs per
+ * 32-row query tile of max_q_len, sequence and KV head; a grid beyond one
+ * launch (2^32 - 1 work-items) returns PKV_ERR_UNSUPPORTED.
  */
 PKV_API int paged_attention_prefill_causal(void *out, int32_t out_dtype, const void *q,
                                    const void *k_cache, const void *v_cache,

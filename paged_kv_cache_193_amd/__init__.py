@@ -20,7 +20,7 @@ Entry points (same names as the C ABI in include/pagedkv.h):
               context_lens, cu_q_lens, scale, max_q_len)
     paged_attention_decode_plan(k_cache, block_tables, context_lens, Hq,
               max_context_len, workspace)
-    paged_attention_decode_workspace_size(...)
+    paged_attention_decode_workspace_size(B, Hq, D, max_context_len, partition_size)
     Scheduler(num_blocks, block_size, max_blocks_per_seq, max_batch, max_step_tokens,
               static_batching=False)  -- pkv_sched_* (host control plane)
 """
@@ -83,7 +83,7 @@ def load_library():
     lib.kv_append_rope.restype = ctypes.c_int
     lib.kv_copy_blocks.argtypes = [P, P, P, P, I, I, I, I, I, P]
     lib.kv_copy_blocks.restype = ctypes.c_int
-    lib.paged_attention_decode_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    lib.paged_attention_decode_workspace_size.argtypes = [I, I, I, I, I]
     lib.paged_attention_decode_workspace_size.restype = Z
     lib.paged_attention_decode.argtypes = [P, I, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I,
                                            P, Z, P]
@@ -159,21 +159,54 @@ def _out_dtype(out):
     raise TypeError("out must be bfloat16 or float32")
 
 
+def _shape(t, n, name):
+    """Shape of t as a tuple of n sizes (ValueError unless t has n dimensions)."""
+    if t.dim() != n:
+        raise ValueError(f"{name} must have {n} dimensions (got shape {tuple(t.shape)})")
+    return tuple(int(x) for x in t.shape)
+
+
+def _pools(k_cache, v_cache):
+    """(N, Hkv, bs, D) of a K/V pool pair of the same shape.  The C ABI sees
+    only pointers, so every size the kernels index with is checked here."""
+    shp = _shape(k_cache, 4, "k_cache")
+    if _shape(v_cache, 4, "v_cache") != shp:
+        raise ValueError(f"v_cache shape {tuple(v_cache.shape)} differs from k_cache {shp}")
+    return shp
+
+
+def _tables(block_tables, context_lens, B):
+    """max_blocks_per_seq of a [B][max_blocks] table, with B context lengths."""
+    nb, maxb = _shape(block_tables, 2, "block_tables")
+    if nb != B:
+        raise ValueError(f"block_tables has {nb} rows for a batch of {B}")
+    if context_lens.numel() != B:
+        raise ValueError(f"context_lens has {context_lens.numel()} entries for a batch of {B}")
+    return maxb
+
+
+def _rows(t, shape, name):
+    if _shape(t, len(shape), name) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
 def kv_append(k_cache, v_cache, k_new, v_new, block_tables, context_lens, cu_new_lens=None):
     """Write new K/V rows [T_new][Hkv][D] into the pools [N][Hkv][bs][D] in place."""
     torch = _torch()
-    N, Hkv, bs, D = k_cache.shape
-    B, maxb = block_tables.shape
-    T_new = k_new.shape[0]
-    if tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(v_new.shape) != tuple(k_new.shape):
-        raise ValueError("k/v shapes differ")
-    if tuple(k_new.shape[1:]) != (Hkv, D):
-        raise ValueError("k_new must be [T_new][Hkv][D]")
+    N, Hkv, bs, D = _pools(k_cache, v_cache)
+    B = _shape(block_tables, 2, "block_tables")[0]
+    maxb = _tables(block_tables, context_lens, B)
+    T_new = _shape(k_new, 3, "k_new")[0]
+    _rows(k_new, (T_new, Hkv, D), "k_new")
+    _rows(v_new, (T_new, Hkv, D), "v_new")
     cu_ptr = None
     if cu_new_lens is not None:
         if cu_new_lens.numel() != B + 1:
             raise ValueError("cu_new_lens must have B+1 entries")
         cu_ptr = _dev(cu_new_lens, torch.int32, "cu_new_lens")
+    elif T_new != B:
+        raise ValueError(f"without cu_new_lens there is one new row per sequence "
+                         f"(T_new {T_new} != B {B})")
     _check(load_library().kv_append(
         _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
         _dev(k_new, torch.bfloat16, "k_new"), _dev(v_new, torch.bfloat16, "v_new"),
@@ -185,9 +218,7 @@ def kv_append(k_cache, v_cache, k_new, v_new, block_tables, context_lens, cu_new
 def kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks):
     """Copy pool block src_blocks[i] onto dst_blocks[i] (int32 device tensors), K and V."""
     torch = _torch()
-    N, Hkv, bs, D = k_cache.shape
-    if tuple(v_cache.shape) != tuple(k_cache.shape):
-        raise ValueError("k/v shapes differ")
+    N, Hkv, bs, D = _pools(k_cache, v_cache)
     n = src_blocks.numel()
     if dst_blocks.numel() != n:
         raise ValueError("src_blocks and dst_blocks differ in length")
@@ -205,13 +236,15 @@ def kv_append_rope(k_cache, v_cache, k_new, v_new, block_tables, context_lens, r
     ([T_new][Hq][D]) is given, the same rotation of q in place.  rope_cos/rope_sin are
     float32 [max_position][D/2] device tables."""
     torch = _torch()
-    N, Hkv, bs, D = k_cache.shape
-    B, maxb = block_tables.shape
-    T_new = k_new.shape[0]
-    if tuple(v_cache.shape) != tuple(k_cache.shape) or tuple(v_new.shape) != tuple(k_new.shape):
-        raise ValueError("k/v shapes differ")
-    if tuple(k_new.shape[1:]) != (Hkv, D):
-        raise ValueError("k_new must be [T_new][Hkv][D]")
+    N, Hkv, bs, D = _pools(k_cache, v_cache)
+    B = _shape(block_tables, 2, "block_tables")[0]
+    maxb = _tables(block_tables, context_lens, B)
+    T_new = _shape(k_new, 3, "k_new")[0]
+    _rows(k_new, (T_new, Hkv, D), "k_new")
+    _rows(v_new, (T_new, Hkv, D), "v_new")
+    if cu_new_lens is None and T_new != B:
+        raise ValueError(f"without cu_new_lens there is one new row per sequence "
+                         f"(T_new {T_new} != B {B})")
     if rope_cos.dim() != 2 or tuple(rope_sin.shape) != tuple(rope_cos.shape) or \
             rope_cos.shape[1] * 2 != D:
         raise ValueError("rope_cos and rope_sin must both be [max_position][D/2]")
@@ -235,10 +268,27 @@ def kv_append_rope(k_cache, v_cache, k_new, v_new, block_tables, context_lens, r
         N, _stream()))
 
 
-def paged_attention_decode_workspace_size(B, Hq, Hkv, D, block_size, max_context_len,
+def paged_attention_decode_workspace_size(B, Hq, D, max_context_len,
                                           partition_size=PARTITION_AUTO) -> int:
     return int(load_library().paged_attention_decode_workspace_size(
-        B, Hq, Hkv, D, block_size, max_context_len, partition_size))
+        int(B), int(Hq), int(D), int(max_context_len), int(partition_size)))
+
+
+def _decode_shapes(out, q, k_cache, v_cache, block_tables, context_lens):
+    """(B, Hq, D, N, Hkv, bs, max_blocks) of a decode call, every size checked."""
+    B, Hq, D = _shape(q, 3, "q")
+    N, Hkv, bs, Dk = _pools(k_cache, v_cache)
+    if Dk != D:
+        raise ValueError(f"pool head_dim {Dk} differs from q's {D}")
+    _rows(out, (B, Hq, D), "out")
+    maxb = _tables(block_tables, context_lens, B)
+    return B, Hq, D, N, Hkv, bs, maxb
+
+
+def _workspace(workspace):
+    if workspace is None:
+        return None, 0
+    return _dev(workspace, _torch().uint8, "workspace"), workspace.numel()
 
 
 def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale,
@@ -248,15 +298,9 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     workspace: a device uint8 tensor of at least
     paged_attention_decode_workspace_size(...) bytes when a split is used."""
     torch = _torch()
-    B, Hq, D = q.shape
-    N, Hkv, bs, _ = k_cache.shape
-    maxb = block_tables.shape[1]
-    if tuple(out.shape) != (B, Hq, D):
-        raise ValueError("out must be [B][Hq][D]")
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        ws_ptr = _dev(workspace, torch.uint8, "workspace")
-        ws_bytes = workspace.numel()
+    B, Hq, D, N, Hkv, bs, maxb = _decode_shapes(out, q, k_cache, v_cache, block_tables,
+                                                context_lens)
+    ws_ptr, ws_bytes = _workspace(workspace)
     _check(load_library().paged_attention_decode(
         _dev(out, out.dtype, "out"), _out_dtype(out), _dev(q, torch.bfloat16, "q"),
         _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
@@ -271,17 +315,11 @@ def paged_attention_decode_append(out, q, k_cache, v_cache, k_new, v_new, block_
     """kv_append of one new token per sequence (k_new/v_new [B][Hkv][D]) followed by
     paged_attention_decode, in one launch for PARTITION_AUTO."""
     torch = _torch()
-    B, Hq, D = q.shape
-    N, Hkv, bs, _ = k_cache.shape
-    maxb = block_tables.shape[1]
-    if tuple(out.shape) != (B, Hq, D):
-        raise ValueError("out must be [B][Hq][D]")
-    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
-        raise ValueError("k_new and v_new must be [B][Hkv][D]")
-    ws_ptr, ws_bytes = None, 0
-    if workspace is not None:
-        ws_ptr = _dev(workspace, torch.uint8, "workspace")
-        ws_bytes = workspace.numel()
+    B, Hq, D, N, Hkv, bs, maxb = _decode_shapes(out, q, k_cache, v_cache, block_tables,
+                                                context_lens)
+    _rows(k_new, (B, Hkv, D), "k_new")
+    _rows(v_new, (B, Hkv, D), "v_new")
+    ws_ptr, ws_bytes = _workspace(workspace)
     _check(load_library().paged_attention_decode_append(
         _dev(out, out.dtype, "out"), _out_dtype(out), _dev(q, torch.bfloat16, "q"),
         _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
@@ -297,8 +335,9 @@ def paged_attention_decode_plan(k_cache, block_tables, context_lens, Hq, max_con
     `workspace` (sized for PARTITION_PLANNED), for decode calls with
     partition_size=PARTITION_PLANNED.  k_cache only supplies the pool shape."""
     torch = _torch()
-    N, Hkv, bs, D = k_cache.shape
-    B, maxb = block_tables.shape
+    N, Hkv, bs, D = _shape(k_cache, 4, "k_cache")
+    B = _shape(block_tables, 2, "block_tables")[0]
+    maxb = _tables(block_tables, context_lens, B)
     _check(load_library().paged_attention_decode_plan(
         _dev(block_tables, torch.int32, "block_tables"),
         _dev(context_lens, torch.int32, "context_lens"), B, Hq, Hkv, D, bs, maxb, N,
@@ -310,11 +349,13 @@ def paged_attention_prefill_causal(out, q, k_cache, v_cache, block_tables, conte
                                    cu_q_lens, scale, max_q_len):
     """out[T][Hq][D] = causal paged prefill attention of packed q[T][Hq][D]."""
     torch = _torch()
-    T, Hq, D = q.shape
-    N, Hkv, bs, _ = k_cache.shape
-    B, maxb = block_tables.shape
-    if tuple(out.shape) != (T, Hq, D):
-        raise ValueError("out must be [T][Hq][D]")
+    T, Hq, D = _shape(q, 3, "q")
+    N, Hkv, bs, Dk = _pools(k_cache, v_cache)
+    if Dk != D:
+        raise ValueError(f"pool head_dim {Dk} differs from q's {D}")
+    _rows(out, (T, Hq, D), "out")
+    B = _shape(block_tables, 2, "block_tables")[0]
+    maxb = _tables(block_tables, context_lens, B)
     if cu_q_lens.numel() != B + 1:
         raise ValueError("cu_q_lens must have B+1 entries")
     _check(load_library().paged_attention_prefill_causal(
@@ -420,11 +461,10 @@ class Scheduler:
         return {k: int(out[i]) for i, k in enumerate(SCHED_STAT_NAMES)}
 
 
-def decode_workspace(B, Hq, Hkv, D, block_size, max_context_len, partition_size, device):
+def decode_workspace(B, Hq, D, max_context_len, partition_size, device):
     """Allocate (with torch) the zero-filled workspace a decode call needs, or
     None.  Later calls leave it zeroed, so it can be reused call after call."""
-    n = paged_attention_decode_workspace_size(B, Hq, Hkv, D, block_size, max_context_len,
-                                              partition_size)
+    n = paged_attention_decode_workspace_size(B, Hq, D, max_context_len, partition_size)
     if n == 0:
         return None
     return _torch().zeros(n, dtype=_torch().uint8, device=device)

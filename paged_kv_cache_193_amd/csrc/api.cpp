@@ -121,8 +121,8 @@ int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new
     return fail(PKV_ERR_INVALID_ARG, "cu_new_lens is NULL but T_new (%d) != B (%d)", T_new, B);
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
     return fail(PKV_ERR_INVALID_ARG, "pools and new rows must be 16-byte aligned");
-  if ((int64_t)T_new * 2 * Hkv * (D / 8) / 256 >= INT32_MAX)
-    return fail(PKV_ERR_UNSUPPORTED, "too many new rows for one launch");
+  if (!pkv::grid_fits(((int64_t)T_new * 2 * Hkv * (D / 8) + 255) / 256, 256))
+    return fail(PKV_ERR_UNSUPPORTED, "too many new rows for one launch (2^32 - 1 work-items)");
   pkv::KvAppendArgs a{k_cache, v_cache, k_new, v_new, block_tables, context_lens, cu_new_lens,
                       B, T_new, Hkv, D, block_size, max_blocks_per_seq, num_blocks};
   return hip_status(pkv::launch_kv_append(a, (hipStream_t)stream), "kv_append launch");
@@ -140,8 +140,8 @@ int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks,
   if (D % 8 != 0) return fail(PKV_ERR_UNSUPPORTED, "D %d is not a multiple of 8", D);
   if (!aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_ERR_INVALID_ARG, "pools must be 16-byte aligned");
-  if ((int64_t)n_pairs * 2 * Hkv * block_size * (D / 8) / 256 >= INT32_MAX)
-    return fail(PKV_ERR_UNSUPPORTED, "too many block copies for one launch");
+  if (!pkv::grid_fits(((int64_t)n_pairs * 2 * Hkv * block_size * (D / 8) + 255) / 256, 256))
+    return fail(PKV_ERR_UNSUPPORTED, "too many block copies for one launch (2^32 - 1 work-items)");
   pkv::CopyBlocksArgs a{k_cache, v_cache, src_blocks, dst_blocks, n_pairs, Hkv, D, block_size,
                         num_blocks};
   return hip_status(pkv::launch_kv_copy_blocks(a, (hipStream_t)stream), "kv_copy_blocks launch");
@@ -171,19 +171,25 @@ int kv_append_rope(void* k_cache, void* v_cache, void* q, const void* k_new, con
       !aligned16(rope_cos) || !aligned16(rope_sin) || (q && !aligned16(q)))
     return fail(PKV_ERR_INVALID_ARG, "pools, rows and rope tables must be 16-byte aligned");
   const int32_t hq = q ? Hq : 0;
-  if ((int64_t)T_new * (hq + 2 * (int64_t)Hkv) * 4 / 256 >= INT32_MAX)
-    return fail(PKV_ERR_UNSUPPORTED, "too many new rows for one launch");
+  if (!pkv::grid_fits(((int64_t)T_new * (hq + 2 * (int64_t)Hkv) * 4 + 255) / 256, 256))
+    return fail(PKV_ERR_UNSUPPORTED, "too many new rows for one launch (2^32 - 1 work-items)");
   pkv::RopeAppendArgs a{k_cache, v_cache, q, k_new, v_new, rope_cos, rope_sin, block_tables,
                         context_lens, cu_new_lens, max_position, B, T_new, hq, Hkv, block_size,
                         max_blocks_per_seq, num_blocks};
   return hip_status(pkv::launch_kv_append_rope(a, (hipStream_t)stream), "kv_append_rope launch");
 }
 
-size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
-                                             int32_t block_size, int32_t max_context_len,
-                                             int32_t partition_size) {
+size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int32_t D,
+                                             int32_t max_context_len, int32_t partition_size) {
+  // The split geometry depends on the KV head count and the block size; this
+  // build implements one GQA group size and one block size, so both follow
+  // from the arguments (a call with any other Hkv or block_size is rejected).
+  if (Hq <= 0 || Hq % kGroup != 0) {
+    fail(PKV_ERR_UNSUPPORTED, "Hq %d is not a multiple of the GQA group %d", Hq, kGroup);
+    return 0;
+  }
   DecodePlan plan;
-  if (plan_decode(B, Hq, Hkv, D, block_size, max_context_len, partition_size, &plan) != PKV_OK)
+  if (plan_decode(B, Hq, Hq / kGroup, D, kBS, max_context_len, partition_size, &plan) != PKV_OK)
     return 0;
   return plan.bytes;
 }
@@ -221,8 +227,10 @@ int prepare_decode(void* out, int32_t out_dtype, const void* q, const void* k_ca
                   workspace ? workspace_bytes : (size_t)0);
     if (!aligned16(workspace)) return fail(PKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
   }
-  if ((int64_t)B * Hkv * plan.parts_max / 4 >= INT32_MAX)
-    return fail(PKV_ERR_UNSUPPORTED, "too many (sequence, head, partition) units for one launch");
+  // one wavefront per (sequence, KV head, partition) unit, four per workgroup
+  if (!pkv::grid_fits(((int64_t)B * Hkv * plan.parts_max + 3) / 4, 256))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "too many (sequence, head, partition) units for one launch (2^32 - 1 work-items)");
   *a = pkv::DecodeArgs{};
   a->out = out;
   a->out_f32 = out_dtype == PKV_OUT_F32;
@@ -371,8 +379,9 @@ int paged_attention_prefill_causal(void* out, int32_t out_dtype, const void* q,
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale must be finite");
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(PKV_ERR_INVALID_ARG, "out, q and the pools must be 16-byte aligned");
-  if (pkv::prefill_grid_size(max_q_len, T_q, B, Hkv) > INT32_MAX)
-    return fail(PKV_ERR_UNSUPPORTED, "%lld workgroups exceed one launch's grid",
+  if (!pkv::grid_fits(pkv::prefill_grid_size(max_q_len, T_q, B, Hkv), 256))
+    return fail(PKV_ERR_UNSUPPORTED, "%lld workgroups of 256 threads exceed one launch "
+                "(at most 2^32 - 1 work-items)",
                 (long long)pkv::prefill_grid_size(max_q_len, T_q, B, Hkv));
   pkv::PrefillArgs a;
   a.out = out;

@@ -93,7 +93,7 @@ hipError_t launch_kv_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream) {
   const int64_t total = (int64_t)a.n_pairs * 2 * chunks;
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
-  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;  // beyond one grid
+  if (!grid_fits(blocks, threads)) return hipErrorInvalidConfiguration;  // beyond one grid
   hipLaunchKernelGGL(kv_copy_blocks_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
                      (uint16_t*)a.k_cache, (uint16_t*)a.v_cache, a.src_blocks, a.dst_blocks,
                      a.n_pairs, chunks, a.num_blocks);
@@ -104,7 +104,7 @@ hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream) {
   const int64_t total = (int64_t)a.T_new * 2 * a.Hkv * (a.D / 8);
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
-  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;  // beyond one grid
+  if (!grid_fits(blocks, threads)) return hipErrorInvalidConfiguration;  // beyond one grid
   hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream,
                      (uint16_t*)a.k_cache, (uint16_t*)a.v_cache, (const uint16_t*)a.k_new,
                      (const uint16_t*)a.v_new, a.block_tables, a.context_lens, a.cu_new_lens,
@@ -220,7 +220,7 @@ hipError_t launch_kv_append_rope(const RopeAppendArgs& a, hipStream_t stream) {
   const int64_t total = (int64_t)a.T_new * (a.Hq + 2 * a.Hkv) * 4;
   const int threads = 256;
   const int64_t blocks = (total + threads - 1) / threads;
-  if (blocks > INT32_MAX) return hipErrorInvalidConfiguration;  // beyond one grid
+  if (!grid_fits(blocks, threads)) return hipErrorInvalidConfiguration;  // beyond one grid
   hipLaunchKernelGGL(kv_append_rope_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }

@@ -8,6 +8,13 @@
 
 namespace pkv {
 
+// A HIP launch on gfx950 covers at most 2^32 - 1 work-items in a dimension
+// (workgroups times threads per workgroup); every grid here is 1-D.
+constexpr int64_t kMaxGridItems = 0xFFFFFFFFll;
+inline bool grid_fits(int64_t workgroups, int threads) {
+  return workgroups >= 0 && workgroups <= kMaxGridItems / threads;
+}
+
 struct KvAppendArgs {
   void* k_cache;
   void* v_cache;

@@ -92,15 +92,24 @@ def test_decode_empty_batch_is_a_noop(lib):
 
 
 def test_decode_workspace_size(lib):
+    """The query takes the contract's (B, Hq, D, max_context_len, partition_size):
+    the KV head count is Hq / 4 and the block size 16 in this build."""
     ws = pkv.paged_attention_decode_workspace_size
-    assert ws(8, 32, 8, 64, 16, 2048, 0) == 0            # no split
-    assert ws(8, 32, 8, 64, 16, 512, 512) == 0           # one partition covers everything
-    rec = 4 * 64 + 8                                      # floats per record
-    counters = 32768 * 128                                # fixed counter region first: one per 128 B
-    assert ws(4, 32, 8, 64, 16, 32768, 512) == counters + 4 * 8 * 64 * rec * 4
-    assert ws(64, 32, 8, 64, 16, 8192, -1) == counters + 2 * 2048 * rec * 4
-    assert ws(4097, 32, 8, 64, 16, 8192, 512) == 0        # too many streams -> rejected
-    assert ws(8, 32, 8, 128, 16, 2048, 512) == 0          # rejected -> 0
+    assert ws(8, 32, 64, 2048, 0) == 0            # no split
+    assert ws(8, 32, 64, 512, 512) == 0           # one partition covers everything
+    rec = 4 * 64 + 8                              # floats per record
+    counters = 32768 * 128                        # fixed counter region first: one per 128 B
+    assert ws(4, 32, 64, 32768, 512) == counters + 4 * 8 * 64 * rec * 4
+    assert ws(64, 32, 64, 8192, -1) == counters + 2 * 2048 * rec * 4
+    assert ws(4, 4, 64, 32768, 512) == counters + 4 * 1 * 64 * rec * 4   # one KV head
+    assert ws(4097, 32, 64, 8192, 512) == 0       # too many streams -> rejected
+    assert ws(8, 32, 128, 2048, 512) == 0         # rejected -> 0
+    assert ws(8, 30, 64, 2048, 512) == 0          # not a multiple of the GQA group
+    assert "GQA group" in pkv.last_error()
+    assert ws(8, 32, 64, 2048, 24) == 0           # not a multiple of the block size
+    assert ws(-1, 32, 64, 2048, 512) == 0
+    # the C prototype has exactly the five arguments
+    assert len(lib.paged_attention_decode_workspace_size.argtypes) == 5
 
 
 def decode_append_call(lib, **kw):
@@ -162,8 +171,8 @@ def test_decode_plan_rejects(lib, kw, code):
 
 def test_planned_workspace_holds_the_plan(lib):
     ws = pkv.paged_attention_decode_workspace_size
-    auto = ws(64, 32, 8, 64, 16, 8192, pkv.PARTITION_AUTO)
-    planned = ws(64, 32, 8, 64, 16, 8192, pkv.PARTITION_PLANNED)
+    auto = ws(64, 32, 64, 8192, pkv.PARTITION_AUTO)
+    planned = ws(64, 32, 64, 8192, pkv.PARTITION_PLANNED)
     plan_ints = 16 + 4097 + 4096 + 2048 * 68
     assert planned == (auto + 255) // 256 * 256 + plan_ints * 4
     assert decode_call(lib, part=pkv.PARTITION_PLANNED) == pkv.PKV_ERR_WORKSPACE
@@ -276,6 +285,8 @@ def prefill_call(lib, **kw):
     (dict(scale=float("nan")), pkv.PKV_ERR_INVALID_ARG),
     # 2^31 - 1 query tokens over 2^20 sequences: more workgroups than one grid
     (dict(B=1 << 20, T=2 ** 31 - 1, maxq=2 ** 31 - 1), pkv.PKV_ERR_UNSUPPORTED),
+    # exactly 2^24 workgroups of 256 threads = 2^32 work-items: one past a launch
+    (dict(B=4096, T=1 << 20, maxq=16384, Hq=32, Hkv=8), pkv.PKV_ERR_UNSUPPORTED),
 ])
 def test_prefill_rejects(lib, kw, code):
     assert prefill_call(lib, **kw) == code
@@ -295,7 +306,7 @@ def test_product_path_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(mod, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(mod, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
-        mod.paged_attention_decode_workspace_size(1, 4, 1, 64, 16, 16, 0)
+        mod.paged_attention_decode_workspace_size(1, 4, 64, 16, 0)
     importlib.reload(pkv)
 
 
@@ -307,3 +318,93 @@ def test_product_package_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
                 assert "liboracle" not in text and "oracle.c" not in text, f
+
+
+def test_append_grid_limit(lib):
+    # 2^32 work-items of kv_append (T_new * 2 * Hkv * D/8): rejected on the host
+    assert append_call(lib, B=1, T=1 << 24, cu=FAKE, Hkv=16, D=64) == pkv.PKV_ERR_UNSUPPORTED
+    assert "2^32" in pkv.last_error()
+
+
+def _cpu_case(B=2, Hq=8, Hkv=2, D=64, N=6, bs=16, maxb=3, T=None):
+    """CPU tensors of a consistent decode/prefill case (never launched: the
+    wrappers reject them, either for a shape or for not being on the device)."""
+    import torch
+    bf = torch.bfloat16
+    T = B if T is None else T
+    return dict(
+        out=torch.zeros((B, Hq, D), dtype=torch.float32), q=torch.zeros((B, Hq, D), dtype=bf),
+        k=torch.zeros((N, Hkv, bs, D), dtype=bf), v=torch.zeros((N, Hkv, bs, D), dtype=bf),
+        kn=torch.zeros((T, Hkv, D), dtype=bf), vn=torch.zeros((T, Hkv, D), dtype=bf),
+        bt=torch.zeros((B, maxb), dtype=torch.int32), cl=torch.ones(B, dtype=torch.int32),
+        cu=torch.arange(B + 1, dtype=torch.int32))
+
+
+def _decode_kw(c, **kw):
+    a = dict(c)
+    a.update(kw)
+    return a
+
+
+@pytest.mark.parametrize("change,match", [
+    (dict(v="short_pool"), "v_cache shape"),
+    (dict(k="short_d", v="short_d"), "head_dim"),
+    (dict(bt="short_table"), "block_tables has"),
+    (dict(cl="short_lens"), "context_lens has"),
+    (dict(out="bad_out"), "out must have shape"),
+    (dict(q="flat_q"), "q must have 3"),
+])
+def test_decode_wrapper_checks_shapes_before_any_launch(lib, change, match):
+    """Sizes the C ABI cannot see are checked in the binding: a smaller V pool,
+    a pool of another head_dim, or a short table or length array would send
+    the kernels past an allocation, so they raise ValueError on the host."""
+    import torch
+    c = _cpu_case()
+    bad = {"short_pool": torch.zeros((3, 2, 16, 64), dtype=torch.bfloat16),
+           "short_d": torch.zeros((6, 2, 16, 32), dtype=torch.bfloat16),
+           "short_table": torch.zeros((1, 3), dtype=torch.int32),
+           "short_lens": torch.ones(1, dtype=torch.int32),
+           "bad_out": torch.zeros((2, 8, 32), dtype=torch.float32),
+           "flat_q": torch.zeros((2, 8 * 64), dtype=torch.bfloat16)}
+    for key, val in change.items():
+        c[key] = bad[val]
+    with pytest.raises(ValueError, match=match):
+        pkv.paged_attention_decode(c["out"], c["q"], c["k"], c["v"], c["bt"], c["cl"], 0.125, 48)
+    with pytest.raises(ValueError, match=match):
+        pkv.paged_attention_decode_append(c["out"], c["q"], c["k"], c["v"], c["kn"], c["vn"],
+                                          c["bt"], c["cl"], 0.125, 48)
+
+
+def test_consistent_cpu_tensors_fail_only_for_the_device(lib):
+    c = _cpu_case()
+    with pytest.raises(ValueError, match="device tensor"):
+        pkv.paged_attention_decode(c["out"], c["q"], c["k"], c["v"], c["bt"], c["cl"], 0.125, 48)
+
+
+def test_append_and_prefill_wrappers_check_shapes(lib):
+    import torch
+    c = _cpu_case(T=5)
+    with pytest.raises(ValueError, match="v_new must have shape"):
+        pkv.kv_append(c["k"], c["v"], c["kn"], c["vn"][:4], c["bt"], c["cl"], c["cu"])
+    with pytest.raises(ValueError, match="context_lens has"):
+        pkv.kv_append(c["k"], c["v"], c["kn"], c["vn"], c["bt"], c["cl"][:1], c["cu"])
+    with pytest.raises(ValueError, match="one new row per sequence"):
+        pkv.kv_append(c["k"], c["v"], c["kn"], c["vn"], c["bt"], c["cl"])
+    with pytest.raises(ValueError, match="v_cache shape"):
+        pkv.kv_append(c["k"], c["v"][:2], c["kn"], c["vn"], c["bt"], c["cl"], c["cu"])
+    cos = torch.zeros((64, 32), dtype=torch.float32)
+    with pytest.raises(ValueError, match="context_lens has 2 entries for a batch of 1"):
+        pkv.kv_append_rope(c["k"], c["v"], c["kn"], c["vn"], c["bt"][:1], c["cl"], cos, cos,
+                           cu_new_lens=c["cu"])
+    q = torch.zeros((5, 8, 64), dtype=torch.bfloat16)
+    out = torch.zeros((5, 8, 64), dtype=torch.float32)
+    with pytest.raises(ValueError, match="head_dim"):
+        pkv.paged_attention_prefill_causal(out, q, c["k"][..., :32].contiguous(),
+                                           c["v"][..., :32].contiguous(), c["bt"], c["cl"],
+                                           c["cu"], 0.125, 4)
+    with pytest.raises(ValueError, match="out must have shape"):
+        pkv.paged_attention_prefill_causal(out[:4], q, c["k"], c["v"], c["bt"], c["cl"], c["cu"],
+                                           0.125, 4)
+    with pytest.raises(ValueError, match="context_lens has"):
+        pkv.paged_attention_prefill_causal(out, q, c["k"], c["v"], c["bt"], c["cl"][:1], c["cu"],
+                                           0.125, 4)

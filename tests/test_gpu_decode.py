@@ -32,7 +32,7 @@ def gpu_decode(c, partition, out_dtype=torch.float32, k=None, v=None, q=None, ta
     lens = dev(c.context_lens) if lens is None else lens
     max_ctx = c.max_context_len if max_ctx is None else max_ctx
     out = torch.full((c.B, c.Hq, c.D), float("nan"), dtype=out_dtype, device="cuda")
-    ws = pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, c.block_size, max_ctx, partition, "cuda")
+    ws = pkv.decode_workspace(c.B, c.Hq, c.D, max_ctx, partition, "cuda")
     pkv.paged_attention_decode(out, q, k, v, tables, lens, c.scale, max_ctx, partition, ws)
     torch.cuda.synchronize()
     return out
@@ -172,7 +172,7 @@ def test_long_context_split_full_size():
     # with the balanced split's plan (as the benchmark times it): the same bits
     k, v = c.extra["k_layers"][0], c.extra["v_layers"][0]
     t, l = dev(c.block_tables), dev(c.context_lens)
-    ws = pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, c.block_size, c.max_context_len,
+    ws = pkv.decode_workspace(c.B, c.Hq, c.D, c.max_context_len,
                               pkv.PARTITION_PLANNED, "cuda")
     pkv.paged_attention_decode_plan(k, t, l, c.Hq, c.max_context_len, ws)
     planned = torch.full_like(auto, float("nan"))
@@ -192,7 +192,7 @@ def test_shared_workspace_reused_across_calls(partition):
     cases = [ragged_case(67, [700, 33, 1, 928, 999]), ragged_case(68, [5, 1024, 64, 300]),
              ragged_case(69, [1024, 1024, 17])]
     refs = [oracle_decode(c) for c in cases]
-    ws = pkv.decode_workspace(5, 32, 8, 64, 16, 1024, partition, "cuda")
+    ws = pkv.decode_workspace(5, 32, 64, 1024, partition, "cuda")
     for rep in range(3):
         for c, ref in zip(cases, refs):
             out = torch.empty((c.B, c.Hq, c.D), dtype=torch.float32, device="cuda")
@@ -219,7 +219,7 @@ def test_largest_batch_of_the_automatic_split():
     ref = oracle.decode(u16(q), u16(k_cache), u16(v_cache), tables.numpy(), lens.numpy(), 0.125)
     k, v, qd, t, l = dev(k_cache), dev(v_cache), dev(q), dev(tables), dev(lens)
     for mode in (pkv.PARTITION_AUTO, pkv.PARTITION_PLANNED):
-        ws = pkv.decode_workspace(B, 32, 8, 64, 16, 40, mode, "cuda")
+        ws = pkv.decode_workspace(B, 32, 64, 40, mode, "cuda")
         if mode == pkv.PARTITION_PLANNED:
             pkv.paged_attention_decode_plan(k, t, l, 32, 40, ws)
         out = torch.full((B, 32, 64), float("nan"), dtype=torch.float32, device="cuda")

@@ -40,7 +40,7 @@ def run_pair(c, partition, out_dtype=torch.float32, max_ctx=None):
         tables, lens = dev(c.block_tables), dev(c.context_lens)
         q, kn, vn = dev(c.q), dev(c.k_new), dev(c.v_new)
         out = torch.full((c.B, c.Hq, c.D), float("nan"), dtype=out_dtype, device="cuda")
-        ws = pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, c.block_size, max_ctx, partition,
+        ws = pkv.decode_workspace(c.B, c.Hq, c.D, max_ctx, partition,
                                   "cuda")
         if fused:
             pkv.paged_attention_decode_append(out, q, k, v, kn, vn, tables, lens, c.scale,
@@ -155,7 +155,7 @@ def test_ragged_full_size_auto():
     for fused in (True, False):
         k, v = k0.clone(), v0.clone()
         out = torch.empty((c.B, c.Hq, c.D), dtype=torch.float32, device="cuda")
-        ws = pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, 16, c.max_context_len,
+        ws = pkv.decode_workspace(c.B, c.Hq, c.D, c.max_context_len,
                                   pkv.PARTITION_AUTO, "cuda")
         if fused:
             pkv.paged_attention_decode_append(out, q, k, v, kn, vn, tables, lens, c.scale,

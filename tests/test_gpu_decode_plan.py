@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 
 def planned_ws(c, max_ctx):
-    return pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, 16, max_ctx, pkv.PARTITION_PLANNED, "cuda")
+    return pkv.decode_workspace(c.B, c.Hq, c.D, max_ctx, pkv.PARTITION_PLANNED, "cuda")
 
 
 def run(c, partition, ws, out_dtype=torch.float32, k=None, v=None, lens=None, tables=None,
@@ -61,7 +61,7 @@ EDGE_LENS = [0, 1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 255, 256, 257, 511, 51
 @pytest.mark.parametrize("case", ["llama1b", "edges"])
 def test_planned_equals_auto(case, out_dtype):
     c = wl.decode_case("llama1b", poison=True) if case == "llama1b" else ragged(81, EDGE_LENS)
-    ws_a = pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, 16, c.max_context_len,
+    ws_a = pkv.decode_workspace(c.B, c.Hq, c.D, c.max_context_len,
                                 pkv.PARTITION_AUTO, "cuda")
     ws_p = planned_ws(c, c.max_context_len)
     auto = run(c, pkv.PARTITION_AUTO, ws_a, out_dtype)
@@ -80,7 +80,7 @@ def test_plan_reused_across_layers_full_size():
     planned call bit-identical to the automatic split; counters stay zero."""
     c = wl.device_decode_case("ragged", "cuda", layers=2)
     tables, lens = dev(c.block_tables), dev(c.context_lens)
-    ws_a = pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, 16, c.max_context_len,
+    ws_a = pkv.decode_workspace(c.B, c.Hq, c.D, c.max_context_len,
                                 pkv.PARTITION_AUTO, "cuda")
     ws_p = planned_ws(c, c.max_context_len)
     pkv.paged_attention_decode_plan(c.extra["k_layers"][0], tables, lens, c.Hq,
@@ -113,7 +113,7 @@ def test_planned_append_equals_two_calls():
             pkv.paged_attention_decode_append(out, q, k, v, kn, vn, tables, lens, c.scale,
                                               c.max_context_len, pkv.PARTITION_PLANNED, ws)
         else:
-            ws = pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, 16, c.max_context_len,
+            ws = pkv.decode_workspace(c.B, c.Hq, c.D, c.max_context_len,
                                       pkv.PARTITION_AUTO, "cuda")
             pkv.kv_append(k, v, kn, vn, tables, lens)
             pkv.paged_attention_decode(out, q, k, v, tables, lens, c.scale, c.max_context_len,
@@ -129,7 +129,7 @@ def test_stale_plan_is_not_used():
     """A plan made before the lengths changed (the next decode step) or for
     another batch size is ignored: the result equals the automatic split."""
     c = ragged(83, [300, 40, 513, 1000])
-    ws_a = pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, 16, 1024, pkv.PARTITION_AUTO, "cuda")
+    ws_a = pkv.decode_workspace(c.B, c.Hq, c.D, 1024, pkv.PARTITION_AUTO, "cuda")
     ws_p = planned_ws(c, 1024)
     tables = dev(c.block_tables)
     pkv.paged_attention_decode_plan(dev(c.k_cache), tables, dev(c.context_lens), c.Hq, 1024, ws_p)
@@ -142,7 +142,7 @@ def test_stale_plan_is_not_used():
     assert torch.equal(bits(a), bits(b))
     # another batch size: the header does not match
     c3 = ragged(84, [77, 900])
-    ws_a3 = pkv.decode_workspace(c3.B, c3.Hq, c3.Hkv, c3.D, 16, 1024, pkv.PARTITION_AUTO, "cuda")
+    ws_a3 = pkv.decode_workspace(c3.B, c3.Hq, c3.D, 1024, pkv.PARTITION_AUTO, "cuda")
     a3 = run(c3, pkv.PARTITION_AUTO, ws_a3, max_ctx=1024)
     b3 = run(c3, pkv.PARTITION_PLANNED, ws_p, max_ctx=1024)
     assert torch.equal(bits(a3), bits(b3))

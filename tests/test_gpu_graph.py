@@ -22,8 +22,8 @@ def test_decode_step_and_prefill_graph_replays():
     kn, vn = dev(c.k_new), dev(c.v_new)
     out_a = torch.empty((c.B, c.Hq, c.D), dtype=torch.float32, device="cuda")
     out_f = torch.empty_like(out_a)
-    ws_a = pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, 16, c.max_context_len, -1, "cuda")
-    ws_f = pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, 16, c.max_context_len, 256, "cuda")
+    ws_a = pkv.decode_workspace(c.B, c.Hq, c.D, c.max_context_len, -1, "cuda")
+    ws_f = pkv.decode_workspace(c.B, c.Hq, c.D, c.max_context_len, 256, "cuda")
     p = wl.prefill_case(prompts=[70, 130], num_blocks=64, seed=81)
     kp, vp = dev(p.k_cache), dev(p.v_cache)
     tp, lp, cu, qp = dev(p.block_tables), dev(p.context_lens), dev(p.cu_q_lens), dev(p.q)
@@ -31,7 +31,7 @@ def test_decode_step_and_prefill_graph_replays():
     out_p = torch.empty(tuple(p.q.shape), dtype=torch.float32, device="cuda")
     k2, v2 = dev(c.k_cache), dev(c.v_cache)
     out_c = torch.empty_like(out_a)
-    ws_c = pkv.decode_workspace(c.B, c.Hq, c.Hkv, c.D, 16, c.max_context_len, -1, "cuda")
+    ws_c = pkv.decode_workspace(c.B, c.Hq, c.D, c.max_context_len, -1, "cuda")
 
     def work():
         pkv.kv_append(k, v, kn, vn, tables, lens)

@@ -30,7 +30,7 @@ def test_scheduled_steps_match_oracle():
     k = torch.full((N, Hkv, bs, D), float("nan"), dtype=torch.bfloat16, device="cuda")
     v = torch.full_like(k, float("nan"))
     k_host, v_host = u16(k.cpu()).copy(), u16(v.cpu()).copy()
-    ws = pkv.decode_workspace(6, Hq, Hkv, D, bs, maxb * bs, pkv.PARTITION_AUTO, "cuda")
+    ws = pkv.decode_workspace(6, Hq, D, maxb * bs, pkv.PARTITION_AUTO, "cuda")
     g = wl.generator(17)
     seen = dict(mixed=0, chunked=0, decode_only=0, preempted=0)
     done = 0
