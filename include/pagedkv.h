@@ -86,6 +86,36 @@ extern "C" {
  */
 PKV_API const char *pagedkv_last_error(void);
 
+/* pagedkv_check_tables -- validate block tables and lengths held in HOST
+ * memory: the data errors the kernels do not check in release builds.
+ *
+ * Defined by: paper-digest page, section "Evidence" (errors that go
+ * unchecked are hard to debug).  With PAGEDKV_DEBUG=1 in the environment,
+ * every kernel entry point copies its tables and lengths to the host (on its
+ * stream, waiting for the copy; not while the stream is being captured into
+ * a graph) and runs this check before launching; a failure returns
+ * PKV_ERR_INVALID_ARG and launches nothing.
+ *
+ * block_tables  [B][max_blocks_per_seq], context_lens [B] (host pointers).
+ * cu_lens       [B+1] prefix sums of new tokens (kind PKV_CHECK_APPEND; NULL
+ *               = one per sequence, T == B) or of query tokens (kind
+ *               PKV_CHECK_PREFILL); ignored when NULL for PKV_CHECK_READ.
+ * T             total new or query tokens (cu_lens[B]).
+ * Checks: 0 <= context_lens[b] <= max_blocks_per_seq * block_size; every
+ * table entry a context uses (ceil(len / block_size) of them) in
+ * [0, num_blocks); prefix sums start at 0, never decrease and end at T; an
+ * append's length is at least its new tokens; a prompt's cached tokens are
+ * at least its query tokens.  Returns PKV_OK or PKV_ERR_INVALID_ARG naming
+ * the first offending sequence in pagedkv_last_error().  Host code only.
+ */
+#define PKV_CHECK_READ 0    /* decode: lengths and the table entries they use */
+#define PKV_CHECK_APPEND 1  /* kv_append: also new-token counts             */
+#define PKV_CHECK_PREFILL 2 /* prefill: also query-token counts             */
+PKV_API int pagedkv_check_tables(const int32_t *block_tables, const int32_t *context_lens,
+                         const int32_t *cu_lens, int32_t B, int32_t T,
+                         int32_t max_blocks_per_seq, int32_t num_blocks,
+                         int32_t block_size, int32_t kind);
+
 /* kv_append -- store the new tokens' K and V rows into the paged pools.
  *
  * Defined by: README table of contents "Why KV cache exists" / "Paged KV

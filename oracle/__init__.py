@@ -210,11 +210,16 @@ _default = None
 
 
 def default() -> Oracle:
+    """The oracle build the module-level functions use: oracle/liboracle.so,
+    or the build PKV_ORACLE_LIB names (the sanitizer build in the CPU tests)."""
     global _default
     if _default is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        _default = Oracle(_build.LIB)
+        path = os.environ.get("PKV_ORACLE_LIB")
+        if not path:
+            if not os.path.exists(_build.LIB):
+                _build.build()
+            path = _build.LIB
+        _default = Oracle(path)
     return _default
 
 

@@ -26,5 +26,18 @@ def build(verbose: bool = False) -> str:
     return compile_source(SRC, LIB, verbose)
 
 
+def build_sanitized(out: str, verbose: bool = False) -> str:
+    """oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer (gcc),
+    for the CPU tests of the sanitizer build; same source, same arithmetic."""
+    cmd = ["gcc", "-std=c99", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-Wall",
+           "-Wextra", SRC, "-o", out + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     build(verbose="-v" in sys.argv)

@@ -39,9 +39,12 @@ PKV_OUT_F32 = 1
 PARTITION_NONE = 0
 PARTITION_AUTO = -1
 PARTITION_PLANNED = -2
+CHECK_READ = 0
+CHECK_APPEND = 1
+CHECK_PREFILL = 2
 
 # every symbol include/pagedkv.h declares
-ABI_SYMBOLS = ("pagedkv_last_error", "kv_append", "kv_append_rope", "kv_copy_blocks",
+ABI_SYMBOLS = ("pagedkv_last_error", "pagedkv_check_tables", "kv_append", "kv_append_rope", "kv_copy_blocks",
                "paged_attention_decode_workspace_size",
                "paged_attention_decode", "paged_attention_decode_append",
                "paged_attention_decode_plan",
@@ -65,6 +68,57 @@ class PagedKVError(RuntimeError):
         self.code = code
 
 
+def _bind_host(lib):
+    """Argument types of the host-only entry points (status text, table
+    checks, scheduler)."""
+    P, I, L = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.pagedkv_last_error.argtypes = []
+    lib.pagedkv_last_error.restype = ctypes.c_char_p
+    lib.pagedkv_check_tables.argtypes = [P, P, P, I, I, I, I, I, I]
+    lib.pagedkv_check_tables.restype = ctypes.c_int
+    lib.pkv_sched_create.argtypes = [I, I, I, I, I, I]
+    lib.pkv_sched_create.restype = P
+    lib.pkv_sched_destroy.argtypes = [P]
+    lib.pkv_sched_destroy.restype = None
+    lib.pkv_sched_add_request.argtypes = [P, L, I, I]
+    lib.pkv_sched_add_request.restype = ctypes.c_int
+    lib.pkv_sched_step.argtypes = [P, P, P, P, P, P]
+    lib.pkv_sched_step.restype = ctypes.c_int
+    lib.pkv_sched_events.argtypes = [P, I, P, I]
+    lib.pkv_sched_events.restype = ctypes.c_int32
+    lib.pkv_sched_stats.argtypes = [P, P]
+    lib.pkv_sched_stats.restype = ctypes.c_int
+    lib.pkv_sched_add_request_prefix.argtypes = [P, L, I, I, L, I]
+    lib.pkv_sched_add_request_prefix.restype = ctypes.c_int
+    lib.pkv_sched_fork.argtypes = [P, L, L, I]
+    lib.pkv_sched_fork.restype = ctypes.c_int
+    lib.pkv_sched_copies.argtypes = [P, P, P, I]
+    lib.pkv_sched_copies.restype = ctypes.c_int32
+
+
+_host_lib = None
+
+
+def host_library():
+    """The library the host-only calls (Scheduler, check_tables) go to:
+    libpagedkv.so, or, when PKV_HOST_LIB names one, a host-only build of the
+    same sources (the sanitizer build the CPU tests use)."""
+    global _host_lib
+    path = os.environ.get("PKV_HOST_LIB")
+    if not path:
+        return load_library()
+    if _host_lib is None or _host_lib._name != path:
+        lib = ctypes.CDLL(path)
+        _bind_host(lib)
+        _host_lib = lib
+    return _host_lib
+
+
+def _check_host(lib, rc):
+    if rc != PKV_OK:
+        raise PagedKVError(rc, lib.pagedkv_last_error().decode())
+
+
 def load_library():
     """Load libpagedkv.so (raises if it has not been built)."""
     global _lib
@@ -75,8 +129,6 @@ def load_library():
                            "(hipcc --offload-arch=gfx950); there is no fallback path")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
-    lib.pagedkv_last_error.argtypes = []
-    lib.pagedkv_last_error.restype = ctypes.c_char_p
     lib.kv_append.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P]
     lib.kv_append.restype = ctypes.c_int
     lib.kv_append_rope.argtypes = [P, P, P, P, P, P, P, I, P, P, P, I, I, I, I, I, I, I, I, P]
@@ -96,25 +148,7 @@ def load_library():
     lib.paged_attention_prefill_causal.argtypes = [P, I, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                    I, I, F, P]
     lib.paged_attention_prefill_causal.restype = ctypes.c_int
-    L = ctypes.c_int64
-    lib.pkv_sched_create.argtypes = [I, I, I, I, I, I]
-    lib.pkv_sched_create.restype = P
-    lib.pkv_sched_destroy.argtypes = [P]
-    lib.pkv_sched_destroy.restype = None
-    lib.pkv_sched_add_request.argtypes = [P, L, I, I]
-    lib.pkv_sched_add_request.restype = ctypes.c_int
-    lib.pkv_sched_step.argtypes = [P, P, P, P, P, P]
-    lib.pkv_sched_step.restype = ctypes.c_int
-    lib.pkv_sched_events.argtypes = [P, I, P, I]
-    lib.pkv_sched_events.restype = ctypes.c_int32
-    lib.pkv_sched_stats.argtypes = [P, P]
-    lib.pkv_sched_stats.restype = ctypes.c_int
-    lib.pkv_sched_add_request_prefix.argtypes = [P, L, I, I, L, I]
-    lib.pkv_sched_add_request_prefix.restype = ctypes.c_int
-    lib.pkv_sched_fork.argtypes = [P, L, L, I]
-    lib.pkv_sched_fork.restype = ctypes.c_int
-    lib.pkv_sched_copies.argtypes = [P, P, P, I]
-    lib.pkv_sched_copies.restype = ctypes.c_int32
+    _bind_host(lib)
     _lib = lib
     return lib
 
@@ -157,6 +191,25 @@ def _out_dtype(out):
     if out.dtype == torch.float32:
         return PKV_OUT_F32
     raise TypeError("out must be bfloat16 or float32")
+
+
+def check_tables(block_tables, context_lens, kind=CHECK_READ, cu_lens=None, block_size=16,
+                 num_blocks=None, T=None):
+    """pagedkv_check_tables on host (numpy) arrays: raises PagedKVError naming
+    the first out-of-range length, block id or prefix sum."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_tables, dtype=np.int32)
+    cl = np.ascontiguousarray(context_lens, dtype=np.int32)
+    cu = None if cu_lens is None else np.ascontiguousarray(cu_lens, dtype=np.int32)
+    B, maxb = bt.shape
+    if cl.shape != (B,) or (cu is not None and cu.shape != (B + 1,)):
+        raise ValueError("context_lens must be [B] and cu_lens [B+1]")
+    if T is None:
+        T = int(cu[-1]) if cu is not None else B
+    p = lambda a: None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+    lib = host_library()
+    _check_host(lib, lib.pagedkv_check_tables(p(bt), p(cl), p(cu), B, int(T), maxb,
+                                              int(num_blocks), int(block_size), int(kind)))
 
 
 def _shape(t, n, name):
@@ -378,7 +431,7 @@ class Scheduler:
                  max_step_tokens, static_batching=False):
         import numpy as np
         self._np = np
-        self._lib = load_library()
+        self._lib = host_library()
         self.max_batch, self.max_blocks_per_seq = max_batch, max_blocks_per_seq
         self._h = self._lib.pkv_sched_create(num_blocks, block_size, max_blocks_per_seq,
                                              max_batch, max_step_tokens,
@@ -457,7 +510,8 @@ class Scheduler:
 
     def stats(self):
         out = self._np.zeros(PKV_SCHED_STATS, dtype=self._np.int64)
-        _check(self._lib.pkv_sched_stats(self._h, out.ctypes.data_as(ctypes.c_void_p)))
+        _check_host(self._lib, self._lib.pkv_sched_stats(self._h,
+                                                         out.ctypes.data_as(ctypes.c_void_p)))
         return {k: int(out[i]) for i, k in enumerate(SCHED_STAT_NAMES)}
 
 

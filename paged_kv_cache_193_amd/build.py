@@ -14,7 +14,10 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libpagedkv.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "pagedkv")
-SOURCES = ["api.cpp", "scheduler.cpp", "kv_append.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "host_checks.cpp", "scheduler.cpp", "kv_append.hip", "decode.hip",
+           "prefill.hip"]
+# host-only sources (no HIP): also built on their own with host sanitizers
+HOST_SOURCES = ["host_checks.cpp", "scheduler.cpp"]
 ARCH = "gfx950"
 
 COMMON = [
@@ -53,6 +56,22 @@ def build(verbose: bool = False, defines=(), lib: str = LIB) -> str:
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose, defines, obj_dir), SOURCES))
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", lib + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(lib + ".tmp", lib)
+    return lib
+
+
+def build_host_sanitized(lib: str, verbose: bool = False) -> str:
+    """The host-only sources (scheduler, table checks, status text) as a
+    shared library built by g++ with AddressSanitizer and
+    UndefinedBehaviorSanitizer, for the CPU tests: no HIP, no device code."""
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-Wall", "-Wextra", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           *[os.path.join(CSRC, s) for s in HOST_SOURCES], "-o", lib + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -8,21 +8,16 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <vector>
 
+#include "errors.h"
 #include "launch.h"
 #include "pagedkv.h"
 
 namespace {
 
-thread_local char g_err[512] = "";
-
-int fail(int code, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_err, sizeof g_err, fmt, ap);
-  va_end(ap);
-  return code;
-}
+using pkv::fail;
 
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return PKV_OK;
@@ -98,11 +93,41 @@ int plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_siz
   return PKV_OK;
 }
 
+// PAGEDKV_DEBUG=1 in the environment: before a launch, copy the call's
+// tables and lengths to the host (on its stream, then wait for them) and
+// validate them with pagedkv_check_tables.  Read at every call, so a process
+// can switch it on and off.  Skipped while the stream is being captured into
+// a graph (a capture cannot wait for a copy).
+bool debug_enabled() {
+  const char* v = getenv("PAGEDKV_DEBUG");
+  return v && v[0] == '1' && v[1] == 0;
+}
+
+int debug_check(const int32_t* block_tables, const int32_t* context_lens, const int32_t* cu_lens,
+                int32_t B, int32_t T, int32_t max_blocks_per_seq, int32_t num_blocks,
+                int32_t kind, hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return PKV_OK;
+  std::vector<int32_t> tables((size_t)B * max_blocks_per_seq), lens(B), cu;
+  hipError_t e = hipMemcpyAsync(tables.data(), block_tables, tables.size() * 4,
+                                hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(lens.data(), context_lens, lens.size() * 4, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess && cu_lens) {
+    cu.resize((size_t)B + 1);
+    e = hipMemcpyAsync(cu.data(), cu_lens, cu.size() * 4, hipMemcpyDeviceToHost, stream);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_status(e, "PAGEDKV_DEBUG copy of tables and lengths");
+  return pagedkv_check_tables(tables.data(), lens.data(), cu_lens ? cu.data() : nullptr, B, T,
+                              max_blocks_per_seq, num_blocks, kBS, kind);
+}
+
 }  // namespace
 
 extern "C" {
 
-const char* pagedkv_last_error(void) { return g_err; }
 
 int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
               const int32_t* block_tables, const int32_t* context_lens,
@@ -123,6 +148,12 @@ int kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new
     return fail(PKV_ERR_INVALID_ARG, "pools and new rows must be 16-byte aligned");
   if (!pkv::grid_fits(((int64_t)T_new * 2 * Hkv * (D / 8) + 255) / 256, 256))
     return fail(PKV_ERR_UNSUPPORTED, "too many new rows for one launch (2^32 - 1 work-items)");
+  if (debug_enabled()) {
+    const int rc = debug_check(block_tables, context_lens, cu_new_lens, B, T_new,
+                               max_blocks_per_seq, num_blocks, PKV_CHECK_APPEND,
+                               (hipStream_t)stream);
+    if (rc != PKV_OK) return rc;
+  }
   pkv::KvAppendArgs a{k_cache, v_cache, k_new, v_new, block_tables, context_lens, cu_new_lens,
                       B, T_new, Hkv, D, block_size, max_blocks_per_seq, num_blocks};
   return hip_status(pkv::launch_kv_append(a, (hipStream_t)stream), "kv_append launch");
@@ -173,6 +204,12 @@ int kv_append_rope(void* k_cache, void* v_cache, void* q, const void* k_new, con
   const int32_t hq = q ? Hq : 0;
   if (!pkv::grid_fits(((int64_t)T_new * (hq + 2 * (int64_t)Hkv) * 4 + 255) / 256, 256))
     return fail(PKV_ERR_UNSUPPORTED, "too many new rows for one launch (2^32 - 1 work-items)");
+  if (debug_enabled()) {
+    const int rc = debug_check(block_tables, context_lens, cu_new_lens, B, T_new,
+                               max_blocks_per_seq, num_blocks, PKV_CHECK_APPEND,
+                               (hipStream_t)stream);
+    if (rc != PKV_OK) return rc;
+  }
   pkv::RopeAppendArgs a{k_cache, v_cache, q, k_new, v_new, rope_cos, rope_sin, block_tables,
                         context_lens, cu_new_lens, max_position, B, T_new, hq, Hkv, block_size,
                         max_blocks_per_seq, num_blocks};
@@ -282,6 +319,11 @@ int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const vo
                                 max_context_len, scale, partition_size, workspace,
                                 workspace_bytes, &a, &nothing);
   if (rc != PKV_OK || nothing) return rc;
+  if (debug_enabled()) {
+    const int rc2 = debug_check(block_tables, context_lens, nullptr, B, 0, max_blocks_per_seq,
+                                num_blocks, PKV_CHECK_READ, (hipStream_t)stream);
+    if (rc2 != PKV_OK) return rc2;
+  }
   return hip_status(pkv::launch_decode(a, (hipStream_t)stream), "paged_attention_decode launch");
 }
 
@@ -303,6 +345,11 @@ int paged_attention_decode_append(void* out, int32_t out_dtype, const void* q, v
   if (!k_new || !v_new) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
   if (!aligned16(k_new) || !aligned16(v_new))
     return fail(PKV_ERR_INVALID_ARG, "new rows must be 16-byte aligned");
+  if (debug_enabled()) {
+    const int rc2 = debug_check(block_tables, context_lens, nullptr, B, B, max_blocks_per_seq,
+                                num_blocks, PKV_CHECK_APPEND, (hipStream_t)stream);
+    if (rc2 != PKV_OK) return rc2;
+  }
   if (a.mode == pkv::kAuto) {  // one launch: the decode kernel stores the new rows
     a.k_new = k_new;
     a.v_new = v_new;
@@ -336,6 +383,11 @@ int paged_attention_decode_plan(const int32_t* block_tables, const int32_t* cont
     return fail(PKV_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", plan.bytes,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned16(workspace)) return fail(PKV_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  if (debug_enabled()) {
+    const int rc2 = debug_check(block_tables, context_lens, nullptr, B, 0, max_blocks_per_seq,
+                                num_blocks, PKV_CHECK_READ, (hipStream_t)stream);
+    if (rc2 != PKV_OK) return rc2;
+  }
   pkv::DecodeArgs a{};
   a.block_tables = block_tables;
   a.context_lens = context_lens;
@@ -383,6 +435,11 @@ int paged_attention_prefill_causal(void* out, int32_t out_dtype, const void* q,
     return fail(PKV_ERR_UNSUPPORTED, "%lld workgroups of 256 threads exceed one launch "
                 "(at most 2^32 - 1 work-items)",
                 (long long)pkv::prefill_grid_size(max_q_len, T_q, B, Hkv));
+  if (debug_enabled()) {
+    const int rc = debug_check(block_tables, context_lens, cu_q_lens, B, T_q, max_blocks_per_seq,
+                               num_blocks, PKV_CHECK_PREFILL, (hipStream_t)stream);
+    if (rc != PKV_OK) return rc;
+  }
   pkv::PrefillArgs a;
   a.out = out;
   a.out_f32 = out_dtype == PKV_OUT_F32;
