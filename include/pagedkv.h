@@ -362,6 +362,33 @@ PKV_API int paged_attention_decode(void *out, int32_t out_dtype, const void *q,
                            int32_t partition_size, void *workspace,
                            size_t workspace_bytes, void *stream);
 
+/* paged_attention_decode_noalloc -- paged_attention_decode without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results and partition modes as paged_attention_decode
+ * except PKV_PARTITION_PLANNED (rejected: the plan lives in a caller
+ * workspace).  The split's counters and partial records live in a static
+ * device array of 16 MiB (PKV_NOALLOC_SCRATCH_BYTES) that each GPU holds
+ * until the process ends; a call whose split needs more
+ * (paged_attention_decode_workspace_size beyond it) returns
+ * PKV_ERR_UNSUPPORTED.  The call allocates nothing: no hipMalloc, hipFree
+ * or allocating library routine.  Its first call on a device zeroes the
+ * counters with a fill kernel on `stream`; every call leaves them at zero
+ * again.  All calls on one GPU share that GPU's array, so calls that
+ * overlap on one GPU (different streams, threads or processes' contexts
+ * excepted) race on it and must be ordered by the caller.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+PKV_API int paged_attention_decode_noalloc(void *out, int32_t out_dtype, const void *q,
+                                   const void *k_cache, const void *v_cache,
+                                   const int32_t *block_tables,
+                                   const int32_t *context_lens, int32_t B, int32_t Hq,
+                                   int32_t Hkv, int32_t D, int32_t block_size,
+                                   int32_t max_blocks_per_seq, int32_t num_blocks,
+                                   int32_t max_context_len, float scale,
+                                   int32_t partition_size, void *stream);
+
 /* paged_attention_decode_plan -- store the plan of the automatic split for
  * these lengths and tables in the workspace, for later calls of
  * paged_attention_decode / _decode_append with PKV_PARTITION_PLANNED.

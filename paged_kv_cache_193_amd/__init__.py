@@ -47,6 +47,7 @@ CHECK_PREFILL = 2
 ABI_SYMBOLS = ("pagedkv_last_error", "pagedkv_check_tables", "kv_append", "kv_append_rope", "kv_copy_blocks",
                "paged_attention_decode_workspace_size",
                "paged_attention_decode", "paged_attention_decode_append",
+               "paged_attention_decode_noalloc",
                "paged_attention_decode_plan",
                "paged_attention_prefill_causal",
                "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_add_request",
@@ -140,6 +141,9 @@ def load_library():
     lib.paged_attention_decode.argtypes = [P, I, P, P, P, P, P, I, I, I, I, I, I, I, I, F, I,
                                            P, Z, P]
     lib.paged_attention_decode.restype = ctypes.c_int
+    lib.paged_attention_decode_noalloc.argtypes = [P, I, P, P, P, P, P, I, I, I, I, I, I, I, I, F,
+                                                   I, P]
+    lib.paged_attention_decode_noalloc.restype = ctypes.c_int
     lib.paged_attention_decode_append.argtypes = [P, I, P, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                   I, F, I, P, Z, P]
     lib.paged_attention_decode_append.restype = ctypes.c_int
@@ -360,6 +364,22 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _dev(block_tables, torch.int32, "block_tables"),
         _dev(context_lens, torch.int32, "context_lens"), B, Hq, Hkv, D, bs, maxb, N,
         int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes, _stream()))
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                   max_context_len, partition_size=PARTITION_AUTO):
+    """paged_attention_decode without a workspace: the split's scratch is the
+    library's static device array (16 MiB per GPU), so the call allocates
+    nothing.  Calls on one GPU share that array and must not overlap."""
+    torch = _torch()
+    B, Hq, D, N, Hkv, bs, maxb = _decode_shapes(out, q, k_cache, v_cache, block_tables,
+                                                context_lens)
+    _check(load_library().paged_attention_decode_noalloc(
+        _dev(out, out.dtype, "out"), _out_dtype(out), _dev(q, torch.bfloat16, "q"),
+        _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
+        _dev(block_tables, torch.int32, "block_tables"),
+        _dev(context_lens, torch.int32, "context_lens"), B, Hq, Hkv, D, bs, maxb, N,
+        int(max_context_len), float(scale), int(partition_size), _stream()))
 
 
 def paged_attention_decode_append(out, q, k_cache, v_cache, k_new, v_new, block_tables,

@@ -8,7 +8,9 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <atomic>
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 
 #include "errors.h"
@@ -301,9 +303,115 @@ int prepare_decode(void* out, int32_t out_dtype, const void* q, const void* k_ca
   return PKV_OK;
 }
 
+// ---- Scratch of paged_attention_decode_noalloc (for callers that cannot
+// allocate): the split's counters and records in a file-scope device array
+// instead of a caller workspace.  Each GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is passed to kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  hipError_t err = hipSuccess;
+  void* ptr = nullptr;              // device address of this device's scratch
+  std::atomic<int> cleared{0};      // the counter region has been zeroed
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+__global__ void zero_words_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// This device's scratch address; on the first call on a device the split
+// counters (which every decode call leaves at zero again) are zeroed on
+// `stream` by a fill kernel first.
+int noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "paged_attention_decode_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(PKV_ERR_UNSUPPORTED, "device %d beyond the %d the scratch table holds", dev,
+                kMaxDevices);
+  ScratchSlot& s = g_scratch[dev];
+  std::call_once(s.once, [&s] {
+    s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch));
+    if (s.err == hipSuccess && !s.ptr) s.err = hipErrorInvalidSymbol;
+  });
+  if (s.err != hipSuccess) return hip_status(s.err, "hipGetSymbolAddress(scratch)");
+  if (s.cleared.exchange(1) == 0) {
+    const int64_t words = (int64_t)pkv::kCounterBytes / 4;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1024), dim3(256), 0, stream,
+                       static_cast<uint32_t*>(s.ptr), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+      s.cleared.store(0);
+      return hip_status(e, "paged_attention_decode_noalloc: scratch fill");
+    }
+  }
+  *out = s.ptr;
+  return PKV_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int paged_attention_decode_noalloc(void* out, int32_t out_dtype, const void* q,
+                                   const void* k_cache, const void* v_cache,
+                                   const int32_t* block_tables, const int32_t* context_lens,
+                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                   int32_t block_size, int32_t max_blocks_per_seq,
+                                   int32_t num_blocks, int32_t max_context_len, float scale,
+                                   int32_t partition_size, void* stream) {
+  if (partition_size == PKV_PARTITION_PLANNED)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "paged_attention_decode_noalloc: a planned split reads its plan from a caller "
+                "workspace; use PKV_PARTITION_AUTO");
+  DecodePlan plan;
+  int rc = plan_decode(B, Hq, Hkv, D, block_size, max_context_len, partition_size, &plan);
+  if (rc != PKV_OK) return rc;
+  if (plan.bytes > kNoAllocScratchBytes)
+    return fail(PKV_ERR_UNSUPPORTED,
+                "paged_attention_decode_noalloc: the split needs %zu bytes of scratch, the "
+                "static scratch holds %zu (use a larger partition_size or "
+                "paged_attention_decode with a workspace)",
+                plan.bytes, kNoAllocScratchBytes);
+  pkv::DecodeArgs a;
+  bool nothing = false;
+  // validate everything before the first HIP call
+  rc = prepare_decode(out, out_dtype, q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv,
+                      D, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                      partition_size, reinterpret_cast<void*>(256), kNoAllocScratchBytes, &a,
+                      &nothing);  // a stand-in workspace address: checks only, no launch
+  if (rc != PKV_OK || nothing) return rc;
+  if (debug_enabled()) {
+    const int rc2 = debug_check(block_tables, context_lens, nullptr, B, 0, max_blocks_per_seq,
+                                num_blocks, PKV_CHECK_READ, (hipStream_t)stream);
+    if (rc2 != PKV_OK) return rc2;
+  }
+  void* ws = nullptr;
+  if (plan.bytes > 0) {
+    rc = noalloc_scratch((hipStream_t)stream, &ws);
+    if (rc != PKV_OK) return rc;
+  }
+  rc = prepare_decode(out, out_dtype, q, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv,
+                      D, block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                      partition_size, ws, ws ? kNoAllocScratchBytes : 0, &a, &nothing);
+  if (rc != PKV_OK) return rc;
+  return hip_status(pkv::launch_decode(a, (hipStream_t)stream),
+                    "paged_attention_decode_noalloc launch");
+}
 
 int paged_attention_decode(void* out, int32_t out_dtype, const void* q, const void* k_cache,
                            const void* v_cache, const int32_t* block_tables,

@@ -408,3 +408,35 @@ def test_append_and_prefill_wrappers_check_shapes(lib):
     with pytest.raises(ValueError, match="context_lens has"):
         pkv.paged_attention_prefill_causal(out, q, c["k"], c["v"], c["bt"], c["cl"][:1], c["cu"],
                                            0.125, 4)
+
+
+def noalloc_call(lib, **kw):
+    a = dict(out=FAKE, out_dtype=pkv.PKV_OUT_F32, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE,
+             B=2, Hq=32, Hkv=8, D=64, bs=16, maxb=4, N=8, maxctx=64, scale=0.125, part=0,
+             stream=None)
+    a.update(kw)
+    return lib.paged_attention_decode_noalloc(a["out"], a["out_dtype"], a["q"], a["k"], a["v"],
+                                              a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                              a["bs"], a["maxb"], a["N"], a["maxctx"], a["scale"],
+                                              a["part"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,match", [
+    (dict(part=pkv.PARTITION_PLANNED), pkv.PKV_ERR_UNSUPPORTED, "plan"),
+    # 256 sequences x 8 heads x 64 partitions of 512: 138 MB of records, over 16 MiB
+    (dict(B=256, maxb=2048, maxctx=32768, part=512), pkv.PKV_ERR_UNSUPPORTED, "static scratch"),
+    (dict(D=128), pkv.PKV_ERR_UNSUPPORTED, "head_dim"),
+    (dict(out=None, part=-1), pkv.PKV_ERR_INVALID_ARG, "null"),
+    (dict(scale=float("nan"), part=-1), pkv.PKV_ERR_INVALID_ARG, "finite"),
+])
+def test_noalloc_rejects_on_the_host(lib, kw, code, match):
+    """Rejections of the no-allocation decode happen before any HIP call."""
+    assert noalloc_call(lib, **kw) == code
+    assert match in pkv.last_error()
+
+
+def test_noalloc_scratch_fits_the_automatic_split(lib):
+    need = pkv.paged_attention_decode_workspace_size(4096, 32, 64, 32768, pkv.PARTITION_AUTO)
+    assert 0 < need <= 16 << 20
+    assert noalloc_call(lib, B=0, out=None, q=None, k=None, v=None, bt=None, cl=None,
+                        part=-1) == pkv.PKV_OK
