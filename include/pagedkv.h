@@ -478,6 +478,33 @@ PKV_API int paged_attention_prefill_causal(void *out, int32_t out_dtype, const v
                                    int32_t num_blocks, int32_t max_q_len, float scale,
                                    void *stream);
 
+/* ---- Measurement.
+ *
+ * pagedkv_stream_blocks -- read, and do nothing else with, the K and V bytes
+ * of whole (block, KV head) chunks of both pools for a list of physical block
+ * ids: the floor a decode call reading the same blocks is measured against.
+ *
+ * Defined by: guide ch. 6 "Prefill vs Decode" (decode is memory bound: it
+ * reads the whole cache once per new token) and ch. 11 "Benchmarks" (state
+ * how close a kernel comes to its bound).  Not part of the attention path.
+ *
+ * block_ids     [n_ids] int32 device array (e.g. every table entry the
+ *               batch's contexts use, in order); ids outside [0, num_blocks)
+ *               read block 0.
+ * k_cache, v_cache  pools as for kv_append; read only.  Every KV head of each
+ *               listed block is read: n_ids * Hkv * block_size * D * 2 bytes
+ *               from each pool.
+ * sink          device buffer of at least PKV_STREAM_SINK_BYTES; receives
+ *               one folded word per lane (meaningless; it keeps the reads).
+ * This build reads 2 KB chunks: D == 64 and block_size == 16.  The grid is
+ * 2048 wavefronts, each streaming an equal contiguous share of the chunks.
+ */
+#define PKV_STREAM_SINK_BYTES (2048u * 64u * 4u)
+PKV_API int pagedkv_stream_blocks(const void *k_cache, const void *v_cache,
+                          const int32_t *block_ids, int32_t n_ids, int32_t Hkv,
+                          int32_t D, int32_t block_size, int32_t num_blocks, void *sink,
+                          size_t sink_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -34,6 +34,26 @@ def _check(rc, what):
         raise ValueError(f"oracle {what}: inputs outside what the tables cover (rc={rc})")
 
 
+def _balanced_groups(items, costs, n):
+    """Deal items out to n groups, heaviest first onto the lightest group."""
+    import heapq
+    groups = [[] for _ in range(n)]
+    heap = [(0, i) for i in range(n)]
+    for c, it in sorted(zip(costs, items), reverse=True):
+        load, i = heapq.heappop(heap)
+        groups[i].append(it)
+        heapq.heappush(heap, (load + max(int(c), 1), i))
+    return [g for g in groups if g]
+
+
+def _in_threads(fn, groups):
+    """fn(group) for every group, one thread each; re-raises the first error."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=len(groups)) as ex:
+        for f in [ex.submit(fn, g) for g in groups]:
+            f.result()
+
+
 class Oracle:
     def __init__(self, path):
         lib = ctypes.CDLL(path)
@@ -73,33 +93,69 @@ class Oracle:
         _check(rc, "kv_append")
 
     def decode(self, q, k_cache, v_cache, block_tables, context_lens, scale,
-               online=False):
-        """q [B][Hq][D] uint16 -> out [B][Hq][D] float64."""
+               online=False, threads=1):
+        """q [B][Hq][D] uint16 -> out [B][Hq][D] float64.
+
+        threads > 1 splits the sequences into that many groups of about equal
+        context (each sequence whole, in one group) and runs the same
+        single-threaded C routine on each group in its own thread (ctypes
+        releases the GIL): the arithmetic of every output is unchanged."""
         q, k_cache, v_cache = _u16(q), _u16(k_cache), _u16(v_cache)
         B, Hq, D = q.shape
         N, Hkv, bs, _ = k_cache.shape
         bt, cl = _i32(block_tables), _i32(context_lens)
         out = np.zeros((B, Hq, D), dtype=np.float64)
         fn = self.lib.oracle_decode_online if online else self.lib.oracle_decode
-        rc = fn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
-                B, Hq, Hkv, D, bs, bt.shape[1], N, float(scale))
-        _check(rc, "decode")
+
+        def run(seqs):
+            for b in seqs:
+                rc = fn(_ptr(out[b:b + 1]), _ptr(q[b:b + 1]), _ptr(k_cache), _ptr(v_cache),
+                        _ptr(bt[b:b + 1]), _ptr(cl[b:b + 1]), 1, Hq, Hkv, D, bs, bt.shape[1],
+                        N, float(scale))
+                _check(rc, "decode")
+
+        if threads <= 1 or B <= 1:
+            rc = fn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
+                    B, Hq, Hkv, D, bs, bt.shape[1], N, float(scale))
+            _check(rc, "decode")
+            return out
+        _in_threads(run, _balanced_groups(list(range(B)), [int(x) + 1 for x in cl], threads))
         return out
 
     def prefill_causal(self, q, k_cache, v_cache, block_tables, context_lens, cu_q_lens,
-                       scale, rows=None):
-        """q [T][Hq][D] uint16 -> out [T][Hq][D] float64 (unlisted rows stay NaN)."""
+                       scale, rows=None, threads=1):
+        """q [T][Hq][D] uint16 -> out [T][Hq][D] float64 (unlisted rows stay NaN).
+
+        threads > 1 deals the rows out to that many threads in groups of
+        about equal cost (visible keys), each running the same single-threaded
+        C routine on its rows; every row's arithmetic is unchanged."""
         q, k_cache, v_cache = _u16(q), _u16(k_cache), _u16(v_cache)
         T, Hq, D = q.shape
         N, Hkv, bs, _ = k_cache.shape
         bt, cl, cu = _i32(block_tables), _i32(context_lens), _i32(cu_q_lens)
         out = np.full((T, Hq, D), np.nan, dtype=np.float64)
         r = None if rows is None else _i32(rows)
-        rc = self.lib.oracle_prefill_causal(
-            _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
-            _ptr(cu), bt.shape[0], Hq, Hkv, D, bs, bt.shape[1], N, float(scale),
-            _ptr(r), 0 if r is None else len(r))
-        _check(rc, "prefill_causal")
+
+        def run(rr):
+            rr = _i32(rr)
+            rc = self.lib.oracle_prefill_causal(
+                _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
+                _ptr(cu), bt.shape[0], Hq, Hkv, D, bs, bt.shape[1], N, float(scale),
+                _ptr(rr), len(rr))
+            _check(rc, "prefill_causal")
+
+        if threads <= 1:
+            rc = self.lib.oracle_prefill_causal(
+                _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(bt), _ptr(cl),
+                _ptr(cu), bt.shape[0], Hq, Hkv, D, bs, bt.shape[1], N, float(scale),
+                _ptr(r), 0 if r is None else len(r))
+            _check(rc, "prefill_causal")
+            return out
+        all_rows = list(range(T)) if r is None else [int(x) for x in r]
+        seq = np.searchsorted(cu, np.asarray(all_rows), side="right") - 1
+        qlen = cu[seq + 1] - cu[seq]
+        cost = (cl[seq] - qlen + (np.asarray(all_rows) - cu[seq]) + 1).tolist()
+        _in_threads(run, _balanced_groups(all_rows, cost, threads))
         return out
 
     def decode_partials(self, q, k_cache, v_cache, block_tables, context_lens, scale,

@@ -49,7 +49,7 @@ ABI_SYMBOLS = ("pagedkv_last_error", "pagedkv_check_tables", "kv_append", "kv_ap
                "paged_attention_decode", "paged_attention_decode_append",
                "paged_attention_decode_noalloc",
                "paged_attention_decode_plan",
-               "paged_attention_prefill_causal",
+               "paged_attention_prefill_causal", "pagedkv_stream_blocks",
                "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_add_request",
                "pkv_sched_step", "pkv_sched_events", "pkv_sched_stats",
                "pkv_sched_add_request_prefix", "pkv_sched_fork", "pkv_sched_copies")
@@ -152,6 +152,8 @@ def load_library():
     lib.paged_attention_prefill_causal.argtypes = [P, I, P, P, P, P, P, P, I, I, I, I, I, I, I,
                                                    I, I, F, P]
     lib.paged_attention_prefill_causal.restype = ctypes.c_int
+    lib.pagedkv_stream_blocks.argtypes = [P, P, P, I, I, I, I, I, P, Z, P]
+    lib.pagedkv_stream_blocks.restype = ctypes.c_int
     _bind_host(lib)
     _lib = lib
     return lib
@@ -438,6 +440,21 @@ def paged_attention_prefill_causal(out, q, k_cache, v_cache, block_tables, conte
         _dev(context_lens, torch.int32, "context_lens"),
         _dev(cu_q_lens, torch.int32, "cu_q_lens"), B, T, Hq, Hkv, D, bs, maxb, N,
         int(max_q_len), float(scale), _stream()))
+
+
+STREAM_SINK_BYTES = 2048 * 64 * 4
+
+
+def stream_blocks(k_cache, v_cache, block_ids, sink):
+    """Measurement probe: read every KV head of the listed pool blocks (int32
+    device tensor) from both pools and nothing else; sink is a uint8 device
+    tensor of at least STREAM_SINK_BYTES."""
+    torch = _torch()
+    N, Hkv, bs, D = _pools(k_cache, v_cache)
+    _check(load_library().pagedkv_stream_blocks(
+        _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
+        _dev(block_ids, torch.int32, "block_ids"), block_ids.numel(), Hkv, D, bs, N,
+        _dev(sink, torch.uint8, "sink"), sink.numel(), _stream()))
 
 
 class Scheduler:

@@ -15,7 +15,7 @@ OUT_DIR = os.path.join(HERE, "_lib")
 LIB = os.path.join(OUT_DIR, "libpagedkv.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "pagedkv")
 SOURCES = ["api.cpp", "host_checks.cpp", "scheduler.cpp", "kv_append.hip", "decode.hip",
-           "prefill.hip"]
+           "prefill.hip", "probe.hip"]
 # host-only sources (no HIP): also built on their own with host sanitizers
 HOST_SOURCES = ["host_checks.cpp", "scheduler.cpp"]
 ARCH = "gfx950"

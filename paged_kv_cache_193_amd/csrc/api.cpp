@@ -569,4 +569,26 @@ int paged_attention_prefill_causal(void* out, int32_t out_dtype, const void* q,
                     "paged_attention_prefill_causal launch");
 }
 
+int pagedkv_stream_blocks(const void* k_cache, const void* v_cache, const int32_t* block_ids,
+                          int32_t n_ids, int32_t Hkv, int32_t D, int32_t block_size,
+                          int32_t num_blocks, void* sink, size_t sink_bytes, void* stream) {
+  if (n_ids < 0) return fail(PKV_ERR_INVALID_ARG, "n_ids must be >= 0 (got %d)", n_ids);
+  if (n_ids == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !block_ids || !sink)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (Hkv <= 0 || num_blocks <= 0)
+    return fail(PKV_ERR_INVALID_ARG, "Hkv and num_blocks must be > 0");
+  if (D != kD || block_size != kBS)
+    return fail(PKV_ERR_UNSUPPORTED, "the streaming probe reads 2 KB chunks: D 64, block_size 16");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(sink))
+    return fail(PKV_ERR_INVALID_ARG, "pools and sink must be 16-byte aligned");
+  const size_t need = (size_t)pkv::stream_blocks_sink_words() * 4;
+  if (sink_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "sink of %zu bytes needed, %zu given", need, sink_bytes);
+  return hip_status(pkv::launch_stream_blocks(k_cache, v_cache, block_ids, n_ids, Hkv, D,
+                                              block_size, num_blocks,
+                                              static_cast<uint32_t*>(sink), (hipStream_t)stream),
+                    "pagedkv_stream_blocks launch");
+}
+
 }  // extern "C"

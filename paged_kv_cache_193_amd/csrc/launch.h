@@ -140,4 +140,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // 32-row query tile of the longest prompt, sequence and KV head).
 int64_t prefill_grid_size(int32_t max_q_len, int32_t T_q, int32_t B, int32_t Hkv);
 
+// Plain streaming read of whole (block, KV head) chunks of both pools for a
+// list of block ids (probe.hip); `sink` receives stream_blocks_sink_words()
+// words.
+int64_t stream_blocks_sink_words();
+hipError_t launch_stream_blocks(const void* k_cache, const void* v_cache, const int32_t* block_ids,
+                                int32_t n_ids, int32_t Hkv, int32_t D, int32_t block_size,
+                                int32_t num_blocks, uint32_t* sink, hipStream_t stream);
+
 }  // namespace pkv

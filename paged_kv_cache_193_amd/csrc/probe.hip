@@ -1,0 +1,80 @@
+// probe.hip -- a plain streaming read of the KV-cache bytes a decode call
+// reads: the floor against which the decode kernel is measured.
+//
+// Decode reads every cached token's K and V row once and is bound by memory
+// bandwidth (nano-vLLM guide announcement, ch. 6 "Prefill vs Decode"); an
+// honest figure for it states how close it comes to simply reading the same
+// bytes (ch. 11 "Benchmarks").  This kernel reads whole (block, KV head)
+// chunks of both pools, 2 KB of K and 2 KB of V each at head_dim 64 and
+// block_size 16, for a list of physical block ids (those the block tables map
+// a batch's contexts to), with no arithmetic beyond folding the words into a
+// register.  The grid is the decode's balanced split grid (2048 wavefronts);
+// each wavefront streams an equal contiguous share of the (block, head)
+// chunks, two chunks in flight, with 16-byte loads that cover whole
+// 128-byte rows.
+#include "device_common.h"
+#include "launch.h"
+
+namespace pkv {
+
+namespace {
+
+constexpr int kProbeWaves = 2048;
+constexpr int kWavesPerGroup = 4;
+
+__global__ void __launch_bounds__(256)
+stream_blocks_kernel(const uint16_t* __restrict__ k_cache, const uint16_t* __restrict__ v_cache,
+                     const int32_t* __restrict__ block_ids, int64_t n_chunks, int Hkv,
+                     int chunk_elems, int num_blocks, uint32_t* __restrict__ sink) {
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * kWavesPerGroup + (threadIdx.x >> 6);
+  const int64_t W = (int64_t)gridDim.x * kWavesPerGroup;
+  const int64_t c0 = w * n_chunks / W, c1 = (w + 1) * n_chunks / W;
+  // lane's 32 bytes of a chunk: elements [16 lane, 16 lane + 16)
+  const int64_t lane_off = (int64_t)lane * 16;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  auto chunk_base = [&](int64_t c) {
+    int id = block_ids[c / Hkv];
+    id = id >= 0 && id < num_blocks ? id : 0;
+    return ((int64_t)id * Hkv + c % Hkv) * chunk_elems + lane_off;
+  };
+  int64_t c = c0;
+  for (; c + 1 < c1; c += 2) {
+    const int64_t a = chunk_base(c), b = chunk_base(c + 1);
+    const u32x4 k0 = *reinterpret_cast<const u32x4*>(k_cache + a);
+    const u32x4 k1 = *reinterpret_cast<const u32x4*>(k_cache + a + 8);
+    const u32x4 v0 = *reinterpret_cast<const u32x4*>(v_cache + a);
+    const u32x4 v1 = *reinterpret_cast<const u32x4*>(v_cache + a + 8);
+    const u32x4 k2 = *reinterpret_cast<const u32x4*>(k_cache + b);
+    const u32x4 k3 = *reinterpret_cast<const u32x4*>(k_cache + b + 8);
+    const u32x4 v2 = *reinterpret_cast<const u32x4*>(v_cache + b);
+    const u32x4 v3 = *reinterpret_cast<const u32x4*>(v_cache + b + 8);
+    acc ^= k0 ^ k1 ^ v0 ^ v1 ^ k2 ^ k3 ^ v2 ^ v3;
+  }
+  if (c < c1) {
+    const int64_t a = chunk_base(c);
+    acc ^= *reinterpret_cast<const u32x4*>(k_cache + a) ^
+           *reinterpret_cast<const u32x4*>(k_cache + a + 8) ^
+           *reinterpret_cast<const u32x4*>(v_cache + a) ^
+           *reinterpret_cast<const u32x4*>(v_cache + a + 8);
+  }
+  // one word per lane, so the loads cannot be dropped
+  sink[w * 64 + lane] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+}
+
+}  // namespace
+
+int64_t stream_blocks_sink_words() { return (int64_t)kProbeWaves * 64; }
+
+hipError_t launch_stream_blocks(const void* k_cache, const void* v_cache, const int32_t* block_ids,
+                                int32_t n_ids, int32_t Hkv, int32_t D, int32_t block_size,
+                                int32_t num_blocks, uint32_t* sink, hipStream_t stream) {
+  const int64_t n_chunks = (int64_t)n_ids * Hkv;
+  hipLaunchKernelGGL(stream_blocks_kernel, dim3(kProbeWaves / kWavesPerGroup),
+                     dim3(kWavesPerGroup * 64), 0, stream, (const uint16_t*)k_cache,
+                     (const uint16_t*)v_cache, block_ids, n_chunks, Hkv, block_size * D,
+                     num_blocks, sink);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

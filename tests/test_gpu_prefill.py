@@ -1,11 +1,13 @@
 """paged_attention_prefill_causal on the GPU vs the CPU oracle.
 
-Small problems are compared on every output; the full workload (prompts
-4 x 512 + 2 x 2048, 32 query / 8 KV heads) on sampled rows the oracle computes
-one by one (first, last and random rows of every prompt).  Bar: max-abs
+Small problems and the full workload (prompts 4 x 512 + 2 x 2048, 32 query /
+8 KV heads) are compared on every output; an 8192-token prompt on the first
+and last row of each of its 256 query tiles plus random rows.  Bar: max-abs
 <= 1e-2, mean-abs <= 1e-3 for fp32 output; bf16 output within max(1e-2,
 1 bf16 ulp) of the oracle rounded to bf16.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -100,20 +102,23 @@ def test_row_equals_decode_at_its_position():
         assert err <= 1e-2, (t, err)
 
 
-def test_full_workload_sampled_rows():
-    """4 x 512 + 2 x 2048 prompts; every prompt's first, last and random rows."""
+def _threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def test_full_workload_every_row():
+    """4 x 512 + 2 x 2048 prompts: every row and head of the output, fp32 and
+    bf16, against the oracle (run on the host's cores, rows dealt out to
+    threads; each row's arithmetic is the oracle's own)."""
     p = wl.prefill_case()
     k, v, kr, vr = appended(p)
-    got = gpu_prefill(p, k, v).cpu().numpy()
-    rng = np.random.default_rng(5)
-    rows = []
-    for b in range(p.B):
-        s, e = int(p.cu_q_lens[b]), int(p.cu_q_lens[b + 1])
-        rows += [s, s + 1, s + 63, s + 64, e - 1, e - 2] + rng.integers(s, e, 6).tolist()
+    print(f"  oracle on {p.q.shape[0]} rows x {p.Hq} heads, {_threads()} threads", flush=True)
     ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
-                                p.cu_q_lens.numpy(), p.scale, rows=rows)
-    assert_close(got[rows], ref[rows], "prefill full sampled")
-    assert np.all(np.isfinite(got))
+                                p.cu_q_lens.numpy(), p.scale, threads=_threads())
+    got = gpu_prefill(p, k, v).cpu().numpy()
+    assert_close(got, ref, "prefill full workload, every row (fp32 out)")
+    got16 = gpu_prefill(p, k, v, torch.bfloat16)
+    assert_close_bf16(got16.cpu(), ref, "prefill full workload, every row")
 
 
 def test_repeatable_bits():
@@ -124,16 +129,20 @@ def test_repeatable_bits():
     assert torch.equal(a, b)
 
 
-def test_long_prompt_sampled_rows():
-    """One 8192-token prompt (128 query tiles, the longest causal range here)
-    checked on sampled rows across the whole prompt."""
+def test_long_prompt_rows_of_every_tile():
+    """One 8192-token prompt (256 query tiles of 32 rows, the longest causal
+    range here): the first and last row of every query tile and 64 random
+    rows, against the oracle."""
     p = wl.prefill_case(prompts=[8192], num_blocks=600, seed=67)
     k, v, kr, vr = appended(p)
     out = gpu_prefill(p, k, v)
-    rows = [0, 1, 63, 64, 65, 2047, 4096, 6000, 8127, 8128, 8190, 8191]
+    rng = np.random.default_rng(67)
+    rows = sorted(set([t * 32 for t in range(256)] + [t * 32 + 31 for t in range(256)]
+                      + rng.integers(0, 8192, 64).tolist()))
     ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
-                                p.cu_q_lens.numpy(), p.scale, rows=rows)
-    assert_close(out.cpu().numpy()[rows], ref[rows], "8192-token prompt, sampled rows")
+                                p.cu_q_lens.numpy(), p.scale, rows=rows, threads=_threads())
+    assert_close(out.cpu().numpy()[rows], ref[rows], f"8192-token prompt, {len(rows)} rows")
+    assert np.all(np.isfinite(out.cpu().numpy()))
 
 
 @pytest.mark.parametrize("slope", [0.15, 0.6, -0.15, -0.6])
