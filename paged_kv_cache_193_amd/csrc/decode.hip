@@ -416,13 +416,10 @@ __device__ __forceinline__ void drain_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Count one stored piece of stream (b, g) (its record stores must have
-// completed: drain_stores()).  The wavefront that completes the count merges
-// all pieces by log-sum-exp and re-zeroes the counter.  Records are read with
-// agent-scope (sc1) loads and the counter is an agent-scope atomic, so pieces
-// written on other XCDs are seen without any cache flush.
 // Add one finished piece to stream (b, g)'s count (agent-scope atomic, issued
-// by lane 0); returns the count before the addition, in every lane.
+// by lane 0; the piece's record stores must have completed: drain_stores())
+// and return the count before the addition, in every lane.  The wavefront
+// whose addition completes the count merges the pieces (merge_streams).
 __device__ __forceinline__ uint32_t count_piece(const Params& p, int b, int g, int lane) {
   uint32_t before = 0;
   if (lane == 0)
