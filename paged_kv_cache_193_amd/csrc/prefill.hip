@@ -13,7 +13,7 @@
 //   O^T[64 d][32 q]     += V^T . P^T     (2 MFMA tiles of 32x32)
 // 32-row query tiles halve the longest unit of work (the last rows of a long
 // prompt see every key tile) and leave room for three workgroups per CU
-// (135 VGPRs, 36 KB of LDS); a one-token row of a mixed batch wastes 31 rows
+// (133 VGPRs, 36 KB of LDS); a one-token row of a mixed batch wastes 31 rows
 // of a tile instead of 63.
 // The MFMA accumulator layout puts one query column and 16 keys in a lane
 // (rows 8*(r/4) + 4*(lane/32) + r%4, column lane%32), which is exactly the
@@ -66,6 +66,7 @@ constexpr int kKRow = kD + 8;      // K and V tile row stride (bf16 elements): 1
 // sends the tile through the exact-max path.  Weights stay below 2^10.
 constexpr float kLazyBound = 1024.f;
 constexpr uint32_t kOnesBf16x2 = 0x3F803F80u;  // bf16 pair (1, 1)
+constexpr int kRsrcWord3 = 0x00020000;         // raw buffer, dword data
 
 struct PParams {
   void* out;
@@ -98,14 +99,16 @@ struct TileRegs {
   u32x4 k0, k1, v0, v1;
 };
 
-// Physical id of the block holding this thread's keys in the tile that starts
-// at key k0 (the logical block index is clamped to the table row, so the read
-// is always in bounds; keys past the context are zeroed by load_tile).
+// Physical id of the block that wavefront `wave` loads for the tile that
+// starts at key k0: the tile's 64 keys are 4 blocks of 16, one per wavefront,
+// so the id is wave-uniform and comes from one scalar load (the logical block
+// index is clamped to the table row, so the read is always in bounds; keys
+// past the context are zeroed by load_tile).
 __device__ __forceinline__ int tile_block_id(const PParams& p, const int32_t* trow, int k0,
-                                             int tid) {
-  int jb = (k0 + 2 * (tid >> 3)) / kBS;
+                                             int wave) {
+  int jb = k0 / kBS + wave;
   jb = jb < p.max_blocks ? jb : p.max_blocks - 1;
-  return trow[jb];
+  return trow[__builtin_amdgcn_readfirstlane(jb)];
 }
 
 // Load this thread's share of the tile at key k0 from block `phys`.  The
@@ -113,15 +116,22 @@ __device__ __forceinline__ int tile_block_id(const PParams& p, const int32_t* tr
 // loads in flight is the same on every path; rows of keys past the context
 // or of an invalid block are replaced by zeros afterwards.
 __device__ __forceinline__ void load_tile(TileRegs& r, const PParams& p, int phys, int g,
-                                          int ctx, int k0, int tid) {
-  const int kp = tid >> 3, c = tid & 7;
+                                          int ctx, int k0, int tid, uint32_t toff) {
+  const int kp = tid >> 3;
   const int key0 = k0 + 2 * kp;  // key0 and key0 + 1 share one 16-token block
+  phys = __builtin_amdgcn_readfirstlane(phys);
   const bool ok = phys >= 0 && phys < p.num_blocks;
-  const int64_t base = (((int64_t)(ok ? phys : 0) * p.Hkv + g) * kBS + (key0 % kBS)) * kD + 8 * c;
-  r.k0 = *reinterpret_cast<const u32x4*>(p.k_cache + base);
-  r.v0 = *reinterpret_cast<const u32x4*>(p.v_cache + base);
-  r.k1 = *reinterpret_cast<const u32x4*>(p.k_cache + base + kD);
-  r.v1 = *reinterpret_cast<const u32x4*>(p.v_cache + base + kD);
+  // one (block, head) chunk of each pool through a buffer descriptor built
+  // in scalar registers: the lane's part of the address is one 32-bit offset
+  const int64_t blk = ((int64_t)(ok ? phys : 0) * p.Hkv + g) * (kBS * kD);
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.k_cache + blk), (short)0, kBS * kD * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(p.v_cache + blk), (short)0, kBS * kD * 2, kRsrcWord3);
+  r.k0 = __builtin_amdgcn_raw_buffer_load_b128(rk, toff * 2, 0, 0);
+  r.v0 = __builtin_amdgcn_raw_buffer_load_b128(rv, toff * 2, 0, 0);
+  r.k1 = __builtin_amdgcn_raw_buffer_load_b128(rk, toff * 2 + kD * 2, 0, 0);
+  r.v1 = __builtin_amdgcn_raw_buffer_load_b128(rv, toff * 2 + kD * 2, 0, 0);
   // Only a tile that reaches past the context holds rows to zero (a wave-
   // uniform test); inside the context the table's ids are valid by contract
   // (an invalid one reads block 0, in bounds, and gives an undefined result).
@@ -218,8 +228,11 @@ prefill_kernel(PParams p) {
   // the block id of the tile after that is read one more tile ahead, so no
   // load waits on a table read.
   TileRegs nxt;
-  int id_next = tile_block_id(p, trow, kTile, tid);
-  load_tile(nxt, p, tile_block_id(p, trow, 0, tid), g, ctx, 0, tid);
+  // this thread's element offset inside a (block, head) chunk: rows
+  // 2 * kp % 16 and the next, head_dim chunk c
+  const uint32_t toff = (uint32_t)((2 * (tid >> 3)) % kBS * kD + 8 * (tid & 7));
+  int id_next = tile_block_id(p, trow, kTile, wave);
+  load_tile(nxt, p, tile_block_id(p, trow, 0, wave), g, ctx, 0, tid, toff);
   store_tile(nxt, ks_buf[0], vs_buf[0], tid);
   __syncthreads();
 
@@ -228,8 +241,8 @@ prefill_kernel(PParams p) {
     const int buf = it & 1;
     // past the last tile these read clamped, unused data (no branch, so the
     // load counts stay static)
-    load_tile(nxt, p, id_next, g, ctx, k0 + kTile, tid);
-    id_next = tile_block_id(p, trow, k0 + 2 * kTile, tid);
+    load_tile(nxt, p, id_next, g, ctx, k0 + kTile, tid, toff);
+    id_next = tile_block_id(p, trow, k0 + 2 * kTile, wave);
     const uint16_t* ks = ks_buf[buf];
     const uint16_t* vs = vs_buf[buf];
 
