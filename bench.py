@@ -3,12 +3,12 @@
 One step = one decode step of the ragged continuous-batching workload:
 64 sequences (context log-uniform in [16, 8192], block_size 16, 65536-block
 bf16 pool per layer, Llama-3.2-1B attention shapes: 32 query heads, 8 KV
-heads, head_dim 64): one paged_attention_decode_plan (the balanced split's
+heads, head_dim 64): one paged_attention_decode_plan (the automatic split's
 plan for this step's lengths and tables, shared by every layer), then for
 each of the 16 layers one
     paged_attention_decode_append(..., PKV_PARTITION_PLANNED)
 call: store one new token per sequence (kv_append) and attend to the whole
-context (paged_attention_decode) with the balanced split, in one kernel
+context (paged_attention_decode) with the automatic split, in one kernel
 launch whose log-sum-exp merge runs inside the kernel.  `--form auto` times
 the same calls without a plan, `--form two-calls` kv_append followed by
 paged_attention_decode per layer.  The step is captured once in a HIP graph
@@ -31,7 +31,7 @@ prefill workload (4 x 512 + 2 x 2048 prompts) on the bf16 MFMA roofline, and
 (kv_append_rope) for the step's 64 new tokens and for the prefill prompts'
 6144, on the HBM roofline.  `long_context` times the long-context split
 workload (4 sequences of 32768 tokens) with fixed 512-token partitions merged
-by log-sum-exp, with the balanced split, and with the balanced split's plan
+by log-sum-exp, with the automatic split, and with the automatic split's plan
 (made once, outside the timed calls), on the HBM roofline.  `mixed_batch`
 times one prefill launch over decode rows and prompt chunks together,
 `copy_blocks` kv_copy_blocks (copy on write), and `scheduler` the host
@@ -77,7 +77,7 @@ def parse():
                     help="planned: one plan per step + combined calls; auto: combined calls "
                          "without a plan; two-calls: kv_append then paged_attention_decode")
     ap.add_argument("--partition", type=int, default=-1,
-                    help="decode partition_size (-1 = automatic balanced split)")
+                    help="decode partition_size (-1 = automatic split)")
     ap.add_argument("--only", choices=("prefill", "long", "mixed", "llama1b"), default=None,
                     help="run this one leg alone and print its JSON object (for profiling "
                          "a single kernel); the contract line is not printed")
@@ -327,8 +327,8 @@ def run_llama1b(torch, pkv, wl, steps, warmup, copies=8):
 def run_long_context(torch, pkv, wl, steps, warmup, copies=4):
     """Long-context split decode: 4 sequences of 32768 tokens, the query of each
     attending to its whole context, with fixed 512-token partitions merged by
-    log-sum-exp (partition_size = 512), with the balanced split, and with the
-    balanced split's plan (made once: the lengths and tables do not change).  `copies`
+    log-sum-exp (partition_size = 512), with the automatic split, and with the
+    automatic split's plan (made once: the lengths and tables do not change).  `copies`
     pool pairs (256 MiB each per pool) are used in turn so that the 256 MB
     last-level cache does not hold the previous call's blocks; returns a dict."""
     dev = "cuda"
@@ -395,7 +395,7 @@ def run_mixed_batch(torch, pkv, wl, steps, warmup, copies=4):
             pkv.paged_attention_prefill_causal(out, q, kc, vc, t, l, cu, p.scale, max(prompts))
     us = graph_us(torch, one_launch, steps, warmup, per_graph=1) / copies
     # the same batch as two launches: the decode rows through
-    # paged_attention_decode (balanced split), the chunks through the prefill
+    # paged_attention_decode (automatic split), the chunks through the prefill
     nd = prompts.count(1)
     out2 = torch.empty_like(out)
     max_dec = max(h + 1 for h in history[:nd])
@@ -463,7 +463,7 @@ def run_mixed_batch(torch, pkv, wl, steps, warmup, copies=4):
             "two_streams_us": round(us3, 2),
             "two_launches_parts_us": {"decode_rows": round(us2_dec, 2),
                                       "prefill_chunks": round(us2_pre, 2)},
-            "two_launches": "decode rows through paged_attention_decode (balanced split), "
+            "two_launches": "decode rows through paged_attention_decode (automatic split), "
                             "then the chunks through paged_attention_prefill_causal; "
                             "two_streams: the same two launches on two streams"}
 

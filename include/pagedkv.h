@@ -71,7 +71,7 @@ extern "C" {
 
 /* partition_size values for paged_attention_decode besides a positive size */
 #define PKV_PARTITION_NONE 0  /* one wavefront per (sequence, KV head)        */
-#define PKV_PARTITION_AUTO (-1) /* balanced split of all blocks over the GPU  */
+#define PKV_PARTITION_AUTO (-1) /* split sized to the batch and the GPU      */
 #define PKV_PARTITION_PLANNED (-2) /* PKV_PARTITION_AUTO from a stored plan      */
 
 /* pagedkv_last_error -- text describing the last non-OK status returned on
@@ -330,9 +330,12 @@ PKV_API size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int3
  *               is split at multiples of that many tokens, partitions run in
  *               parallel and the wavefront that finishes a sequence's last
  *               partition merges them by log-sum-exp (no second kernel).
- *               PKV_PARTITION_AUTO: all blocks of the batch are cut into equal
- *               shares, one per wavefront of a fixed grid, and streams cut
- *               across shares are merged the same way.
+ *               PKV_PARTITION_AUTO: each (sequence, KV head) is cut into
+ *               pieces of equal length, no longer than a bound chosen from
+ *               the batch's total length so that there is about one piece
+ *               per wavefront of the grid (2048 wavefronts, or 512 plus one
+ *               per (sequence, KV head) when there are more than 1536 of
+ *               them), and pieces are merged the same way.
  *               PKV_PARTITION_PLANNED: the same split, read from a plan that
  *               paged_attention_decode_plan stored in this workspace (see
  *               there); a plan made for other B, Hkv, max_blocks_per_seq,
@@ -348,7 +351,8 @@ PKV_API size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int3
  *               must not run concurrently (they would race on it).  Splits
  *               handle up to 32768 (sequence, KV head) streams and up to
  *               2^21 - 1 partial records (B * Hkv * partitions per sequence
- *               for a fixed partition_size, 4096 for PKV_PARTITION_AUTO);
+ *               for a fixed partition_size, one per wavefront of the grid
+ *               for PKV_PARTITION_AUTO);
  *               beyond either limit the call returns PKV_ERR_UNSUPPORTED.
  * This build implements D == 64, block_size == 16 and Hq == 4 * Hkv
  * (PKV_ERR_UNSUPPORTED otherwise).  Empty contexts give zero rows.
@@ -398,9 +402,9 @@ PKV_API int paged_attention_decode_noalloc(void *out, int32_t out_dtype, const v
  * tables and lengths).
  *
  * The plan is what the automatic split computes before its first key load:
- * the prefix of per-sequence block counts, and for each wavefront of its
- * fixed grid the stream it starts in and the block ids of its first 64 list
- * positions.  Every layer of a decode step shares block_tables and
+ * its piece bound, the prefix of per-sequence piece counts, and for each
+ * wavefront of its grid the piece it attends over and the block ids of that
+ * piece's first 64 blocks.  Every layer of a decode step shares block_tables and
  * context_lens, so one plan per step serves all of them and each call starts
  * loading keys at once.  A plan describes the contents of block_tables and
  * context_lens at the time of this call: after they change (the next step),

@@ -90,7 +90,7 @@ int plan_decode(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t block_siz
   }
   if (plan->planned) {
     plan->plan_offset = (plan->bytes + 255) / 256 * 256;
-    plan->bytes = plan->plan_offset + pkv::kPlanBytes;
+    plan->bytes = plan->plan_offset + pkv::plan_bytes((int64_t)B * Hkv);
   }
   return PKV_OK;
 }

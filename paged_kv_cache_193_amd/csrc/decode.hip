@@ -638,94 +638,27 @@ decode_units_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------
-// kAuto: balanced split over a fixed grid of kAutoWaves wavefronts.
+// kAuto: stream-aligned pieces, one per wavefront.
 //
-// Every stream (b, g) is padded to a multiple of kRing blocks and all streams,
-// in (b, g) order, form one global block list whose ring groups are dealt out
-// as evenly as possible (shares differ by at most one group), one share per
-// wavefront.  So every ring group of kRing
-// blocks lies inside one stream, padding blocks are masked (their loads re-read
-// a real block of the stream), and a wavefront streams its share through ONE
-// continuous ring across stream boundaries: the next group's block ids (scalar
-// loads) and query rows (vector loads) are fetched one group ahead, so a new
-// stream costs no pipeline drain.  A share holds at most two partial streams
-// (its first and last segment); streams strictly inside it are complete and
-// written directly.  Record slots: wavefront w owns records 2w (first segment)
-// and 2w+1 (last segment).
-
-// First block of wavefront w's share when gbase groups go to every
-// wavefront and one more to the first `rem`.
-__device__ __forceinline__ int64_t share_start(int64_t w, int64_t gbase, int64_t rem) {
-  return (int64_t)kRing * (w * gbase + (w < rem ? w : rem));
-}
-
-// Wavefront whose share holds block x.
-__device__ __forceinline__ int64_t share_of(int64_t x, int64_t gbase, int64_t rem) {
-  const int64_t gx = x / kRing;
-  const int64_t big = rem * (gbase + 1);
-  if (gx < big) return gx / (gbase + 1);
-  return rem + (gx - big) / gbase;
-}
-
-__device__ __forceinline__ int padded_blocks(int ctx) {
-  const int nb = (ctx + kBS - 1) / kBS;
-  return (nb + kRing - 1) / kRing * kRing;
-}
-
-// Position in the padded block list; every field is wave-uniform.
-struct Cursor {
-  int b, g, j;      // stream (b, g), block j of it (a multiple of kRing)
-  int nbp, nbr;     // padded and real block counts of the stream
-  int ctx;          // context length of sequence b
-};
-
-__device__ __forceinline__ void cursor_load_seq(Cursor& c, const int* s_ctx, int b) {
-  c.b = b;
-  c.ctx = __builtin_amdgcn_readfirstlane(s_ctx[b]);
-  c.nbr = (c.ctx + kBS - 1) / kBS;
-  c.nbp = (c.nbr + kRing - 1) / kRing * kRing;
-}
-
-// Move one ring group forward (only called while the target is inside the
-// list, so b stays below B).
-__device__ __forceinline__ void cursor_advance(Cursor& c, const int* s_ctx, int Hkv, int B) {
-  c.j += kRing;
-  if (c.j < c.nbp) return;
-  c.j = 0;
-  if (++c.g < Hkv) return;
-  c.g = 0;
-  int b = c.b + 1;
-  while (b < B - 1 && __builtin_amdgcn_readfirstlane(s_ctx[b]) == 0) ++b;
-  cursor_load_seq(c, s_ctx, b < B ? b : B - 1);  // b < B whenever a group follows
-}
-
-// Block-id window: lane k returns the physical id of block xs + k of the
-// padded list (the cursor c sits at xs), clamped to its stream's last real
-// block; 0 past x1.  One vector load per 64 blocks; ids are then read with
-// readlane, so no scalar-load wait ever sits between two ring groups.
-__device__ __forceinline__ int id_window(const Params& p, const int* s_ctx, const Cursor& c,
-                                         int64_t xs, int64_t x1, int lane) {
-  if (xs + lane >= x1) return 0;
-  int b = c.b, g = c.g, j = c.j, nbp = c.nbp, nbr = c.nbr;
-  int k = lane;
-  while (k >= nbp - j) {
-    k -= nbp - j;
-    j = 0;
-    if (++g == p.Hkv) {
-      g = 0;
-      do {
-        ++b;
-      } while (b < p.B - 1 && s_ctx[b] == 0);
-      if (b >= p.B) return -1;  // not reached while the list holds xs + lane
-      nbr = (s_ctx[b] + kBS - 1) / kBS;
-      nbp = (nbr + kRing - 1) / kRing * kRing;
-    }
-  }
-  if (nbr <= 0) return -1;  // not reached: streams without blocks are not in the list
-  j += k;
-  const int jj = j < nbr - 1 ? j : nbr - 1;
-  return p.block_tables[(int64_t)b * p.max_blocks + jj];
-}
+// The batch's blocks are cut into pieces, each inside one stream (sequence b,
+// KV head g).  A piece holds at most P blocks, the smallest bound that leaves
+// one wavefront per stream spare,
+//     P = max(kMinPiece, ceil(NB * Hkv / max(W - S, W / 4))),
+// for NB blocks over the sequences, S = B * Hkv streams and W = kAutoWaves.  A
+// stream of nb blocks is cut into u = ceil(nb / P) pieces of equal length
+// (piece k: blocks [k nb / u, (k + 1) nb / u)); an empty stream is one piece
+// that writes zero rows.  That makes at most W pieces when S <= 3W/4 and at
+// most W/4 + S otherwise; the grid has that many wavefronts (auto_waves), and
+// wavefront w takes piece w of the numbering stream by stream in (b, g)
+// order.  A piece loads its stream's queries once and runs its own ring of
+// kRing blocks, so nothing crosses a stream boundary.  A piece that is a
+// whole stream writes the output rows; the pieces of a cut stream write
+// records, numbered over the cut streams only, and the last of a stream to
+// finish merges them.  A cut stream has nb > P blocks and fewer than 2 nb / P
+// pieces, so there are fewer than 2 * max(W - S, W / 4) <= 2W records.
+// Pieces shorter than kMinPiece blocks would cost more in start-up and
+// merging than their parallelism gains.
+constexpr int kMinPiece = 8;
 
 __device__ __forceinline__ void load_q(uint32_t (&qv)[4][4], const Params& p, int b, int g,
                                        int i, int c) {
@@ -755,37 +688,54 @@ __device__ __forceinline__ void reset_state(LaneState& st) {
     for (int e = 0; e < 8; ++e) st.acc[j][e] = 0.f;
 }
 
-// Stream and block of list position x0: largest b with Hkv * pfx[b] <= x0.
-__device__ __forceinline__ void locate_share(Cursor& cc, const Params& p, const int* pfx,
-                                             const int* s_ctx, int64_t x0) {
-  int lo = 0, hi = p.B;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if ((int64_t)p.Hkv * pfx[mid] <= x0) lo = mid; else hi = mid;
-  }
-  cursor_load_seq(cc, s_ctx, __builtin_amdgcn_readfirstlane(lo));
-  const int64_t off = x0 - (int64_t)p.Hkv * __builtin_amdgcn_readfirstlane(pfx[cc.b]);
-  cc.g = (int)(off / cc.nbp);
-  cc.j = (int)(off - (int64_t)cc.g * cc.nbp);
+
+__device__ __forceinline__ int piece_bound(int64_t nb_total, int B, int Hkv, int W) {
+  const int64_t S = (int64_t)B * Hkv;
+  const int64_t spare = W - S > W / 4 ? W - S : W / 4;
+  const int64_t P = (nb_total * Hkv + spare - 1) / spare;
+  return P < kMinPiece ? kMinPiece : (int)(P < (1 << 30) ? P : (1 << 30));
 }
 
-// Context lengths (clamped) of all sequences and the exclusive prefix of
-// their padded block counts, in LDS (pfx[B] = total); with kAppend also
-// whether each sequence's new token is stored by the wavefronts.
+__device__ __forceinline__ int pieces_of(int nb, int P) { return nb == 0 ? 1 : (nb + P - 1) / P; }
+
+// Per-sequence prefix word: pieces before the sequence (per KV head) in the
+// low 16 bits, records of cut streams before it (per KV head) in the high 16.
+// Both totals stay below 2^16 (at most W/4 + B <= 4608 pieces and fewer than
+// 2W = 4096 records per KV head), so the two fields add without carrying
+// into each other.
+__device__ __forceinline__ int prefix_word(int nb, int P) {
+  const int n = pieces_of(nb, P);
+  return n | ((n > 1 ? n : 0) << 16);
+}
+__device__ __forceinline__ int pu_pieces(int w) { return w & 0xFFFF; }
+__device__ __forceinline__ int pu_records(int w) { return (int)((unsigned)w >> 16); }
+
+// Context lengths (clamped) of all sequences in LDS, the piece bound P
+// (returned) and the exclusive prefix words of the sequences (pu[B]: the
+// totals); with kAppend also whether each sequence's new token is read by
+// its stream's last piece.
 template <bool kAppend>
-__device__ __forceinline__ void block_prefix(const Params& p, int* pfx, int* s_ctx,
-                                             unsigned char* s_newok, int* wsum, int tid,
-                                             int lane, int wave) {
+__device__ __forceinline__ int piece_prefix(const Params& p, int* pu, int* s_ctx,
+                                            unsigned char* s_newok, int* wsum,
+                                            long long* wtot, int tid, int lane, int wave) {
   const int per = (p.B + kWaves * 64 - 1) / (kWaves * 64);
   const int beg = tid * per;
   const int end = beg + per < p.B ? beg + per : p.B;
-  int local = 0;
+  long long nbs = 0;
   for (int k = beg; k < end; ++k) {
     const int c = eff_ctx(p, k);
     s_ctx[k] = c;
     if (kAppend) s_newok[k] = c >= 1 && c == p.context_lens[k];
-    local += padded_blocks(c);
+    nbs += (c + kBS - 1) / kBS;
   }
+  for (int off = 32; off >= 1; off >>= 1) nbs += __shfl_xor(nbs, off);
+  if (lane == 0) wtot[wave] = nbs;
+  __syncthreads();
+  long long tot = 0;
+  for (int w2 = 0; w2 < kWaves; ++w2) tot += wtot[w2];
+  const int P = piece_bound(tot, p.B, p.Hkv, kAutoWaves);
+  int local = 0;
+  for (int k = beg; k < end; ++k) local += prefix_word((s_ctx[k] + kBS - 1) / kBS, P);
   int incl = local;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -797,148 +747,309 @@ __device__ __forceinline__ void block_prefix(const Params& p, int* pfx, int* s_c
   int run = incl - local;
   for (int w2 = 0; w2 < wave; ++w2) run += wsum[w2];
   for (int k = beg; k < end; ++k) {
-    pfx[k] = run;
-    run += padded_blocks(s_ctx[k]);
+    pu[k] = run;
+    run += prefix_word((s_ctx[k] + kBS - 1) / kBS, P);
   }
-  if (tid == kWaves * 64 - 1) pfx[p.B] = run;
+  if (tid == kWaves * 64 - 1) pu[p.B] = run;
   __syncthreads();
+  return P;
 }
 
-// The plan of the balanced split for this call's lengths and tables: what
-// decode_auto_kernel computes before its first load (the prefix of padded
-// block counts, each wavefront's first stream and the block ids of its first
-// 64 list positions), stored once so that calls which share lengths and
-// tables (every layer of a decode step) start loading keys at once.
+// Piece u of the numbering: its stream (b, g), its blocks [j0, j1), its
+// index k in the stream, the stream's piece count and (cut streams) the
+// record number of the stream's first piece.
+struct Piece {
+  int b, g, j0, j1, ctx, pieces, base, k;
+};
+
+__device__ __forceinline__ Piece locate_piece(const Params& p, const int* pu, const int* s_ctx,
+                                              int64_t u) {
+  int lo = 0, hi = p.B;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)p.Hkv * pu_pieces(pu[mid]) <= u) lo = mid; else hi = mid;
+  }
+  Piece pc;
+  pc.b = __builtin_amdgcn_readfirstlane(lo);
+  const int w0 = __builtin_amdgcn_readfirstlane(pu[pc.b]);
+  const int first = pu_pieces(w0);
+  pc.pieces = pu_pieces(__builtin_amdgcn_readfirstlane(pu[pc.b + 1])) - first;
+  const int off = (int)(u - (int64_t)p.Hkv * first);
+  pc.g = off / pc.pieces;
+  pc.k = off - pc.g * pc.pieces;
+  pc.ctx = __builtin_amdgcn_readfirstlane(s_ctx[pc.b]);
+  const int nb = (pc.ctx + kBS - 1) / kBS;
+  pc.j0 = (int)((int64_t)pc.k * nb / pc.pieces);
+  pc.j1 = (int)((int64_t)(pc.k + 1) * nb / pc.pieces);
+  pc.base = p.Hkv * pu_records(w0) + pc.g * pc.pieces;
+  return pc;
+}
+
+// Block ids of a piece: lane k holds the id of block j0 + k, clamped to the
+// piece's last block.
+__device__ __forceinline__ int piece_ids(const Params& p, const Piece& pc, int from, int lane) {
+  const int last = pc.j1 - 1;
+  const int j = from + lane < last ? from + lane : last;
+  return p.block_tables[(int64_t)pc.b * p.max_blocks + j];
+}
+
+// A piece in flight: its ring of kRing blocks (their valid token counts, V
+// offsets and, for the append, whether a slot holds the stream's last block),
+// its block-id window, its queries and (append) this lane's chunks of the new
+// token's K and V rows.
+struct PieceRun {
+  BlockRegs ring[kRing];
+  int nvalid[kRing];
+  int64_t ub[kRing];
+  bool slast[kRing];
+  uint32_t qv[4][4];
+  int tab, tab_base;
+  int last_phys;
+  u32x4 knv, vnv;
+};
+
+// Load the piece's queries (and, for the piece that holds its stream's last
+// block, the new token's chunks) and issue its first group of blocks; `tab`
+// is its block-id window from block j0.
+template <bool kAppend>
+__device__ __forceinline__ void piece_begin(PieceRun& r, const Params& p, const Piece& pc,
+                                            int tab, int lane) {
+  const int grp = lane >> 3, i = lane & 7;
+  const bool quad1 = (i & 4) != 0;
+  const int c = quad1 ? ((i & 3) ^ 3) : (i & 3);
+  const int lane_off = grp * kD + 8 * i;
+  const int nb = (pc.ctx + kBS - 1) / kBS;
+  load_q(r.qv, p, pc.b, pc.g, i, c);
+  if (kAppend && pc.j1 == nb) load_new(r.knv, r.vnv, p, pc.b, pc.g, i);
+  r.tab = tab;
+  r.tab_base = pc.j0;
+  r.last_phys = 0;
+  const int last = pc.j1 - 1;
+#pragma unroll
+  for (int s = 0; s < kRing; ++s) {
+    const int j = pc.j0 + s < last ? pc.j0 + s : last;
+    const int id = __builtin_amdgcn_readlane(tab, j - pc.j0);
+    int64_t ub;
+    const int nv = issue_k(r.ring[s], p, id, pc.g, j, pc.ctx, lane_off, ub);
+    issue_v(r.ring[s], p, ub, lane_off);
+    r.nvalid[s] = pc.j0 + s < pc.j1 ? nv : 0;
+    if (kAppend) {
+      r.slast[s] = pc.j0 + s == nb - 1 && nv > 0;
+      if (r.slast[s]) r.last_phys = id;
+    }
+  }
+}
+
+// Run the piece's blocks through its ring (as run_segment); with `app` the
+// new token's rows replace the stale ones its last block returned and are
+// stored to the pools.
+template <bool kAppend>
+__device__ __forceinline__ void piece_run(LaneState& st, PieceRun& r, const Params& p,
+                                          const Piece& pc, bool app, int lane) {
+  const int grp = lane >> 3, i = lane & 7;
+  const bool quad1 = (i & 4) != 0;
+  const int own_tok = quad1 ? grp + 8 : grp;
+  const int lane_off = grp * kD + 8 * i;
+  reset_state(st);
+  const int32_t* trow = p.block_tables + (int64_t)pc.b * p.max_blocks;
+  const int nb = (pc.ctx + kBS - 1) / kBS;
+  const int n = pc.j1 - pc.j0;
+  const int last = pc.j1 - 1;
+  const int t_new = (pc.ctx - 1) & (kBS - 1);
+  for (int base = 0; base < n; base += kRing) {
+    if (kAppend && app) {
+#pragma unroll
+      for (int s = 0; s < kRing; ++s) {
+        if (r.slast[s]) {
+          if (grp == t_new) r.ring[s].ka = r.knv;
+          if (grp + 8 == t_new) r.ring[s].kb = r.knv;
+          if (grp == (t_new & 7)) {
+            const int64_t off = (((int64_t)r.last_phys * p.Hkv + pc.g) * kBS + t_new) * kD + 8 * i;
+            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_cache) + off) = r.knv;
+            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_cache) + off) = r.vnv;
+          }
+        }
+      }
+    }
+    bool full = true;
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) full = full && r.nvalid[s] == kBS;
+    float x[kRing];
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+      x[s] = block_score(r.ring[s], r.qv, p.scale_log2, quad1);
+      if (!full && own_tok >= r.nvalid[s]) x[s] = -INFINITY;
+    }
+    // the K halves of the slots are free: refill them with the blocks kRing
+    // ahead (their V halves follow each slot's P.V)
+    int nv_next[kRing];
+    bool sl_next[kRing];
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+      const int jn = pc.j0 + base + s + kRing;
+      const int j = jn < last ? jn : last;
+      if (j - r.tab_base >= 64) {
+        r.tab_base += 64;
+        r.tab = trow[r.tab_base + lane < last ? r.tab_base + lane : last];
+        // wait here (vmcnt 0), inside the branch, so the common path after it
+        // carries no wait for this load
+        __builtin_amdgcn_s_waitcnt(0x0F70);
+      }
+      const int id = __builtin_amdgcn_readlane(r.tab, j - r.tab_base);
+      const int nv = issue_k(r.ring[s], p, id, pc.g, j, pc.ctx, lane_off, r.ub[s]);
+      nv_next[s] = jn < pc.j1 ? nv : 0;
+      if (kAppend) {
+        sl_next[s] = jn == nb - 1 && jn < pc.j1 && nv > 0;
+        if (sl_next[s]) r.last_phys = id;
+      }
+    }
+    // one max per group, shared by the mirror pair (same head, tokens t, t+8)
+    float mx = x[0];
+#pragma unroll
+    for (int s = 1; s < kRing; ++s) mx = fmaxf(mx, x[s]);
+    mx = fmaxf(mx, dpp<kRowHalfMirror>(mx));
+    const float m_new = fmaxf(st.m, mx);
+    // no valid token yet on this lane pair: keep everything at zero weight
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+    st.m = m_new;
+    st.l *= alpha;
+    const float a1 = dpp<kQuadXor1>(alpha), a2 = dpp<kQuadXor2>(alpha),
+                a3 = dpp<kQuadXor3>(alpha);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      st.acc[0][e] *= alpha;
+      st.acc[1][e] *= a1;
+      st.acc[2][e] *= a2;
+      st.acc[3][e] *= a3;
+    }
+#pragma unroll
+    for (int s = 0; s < kRing; ++s) {
+      const float pw = __builtin_amdgcn_exp2f(x[s] - m_use);  // 0 for x = -inf
+      st.l += pw;
+      if (kAppend && app && r.slast[s]) {
+        if (grp == t_new) r.ring[s].va = r.vnv;
+        if (grp + 8 == t_new) r.ring[s].vb = r.vnv;
+      }
+      if (full)
+        block_pv<false>(st, r.ring[s], pw, quad1, true, true);
+      else
+        block_pv<true>(st, r.ring[s], pw, quad1, grp < r.nvalid[s], grp + 8 < r.nvalid[s]);
+      issue_v(r.ring[s], p, r.ub[s], lane_off);
+      r.nvalid[s] = nv_next[s];
+      if (kAppend) r.slast[s] = sl_next[s];
+    }
+  }
+}
+
+// The plan of the split for this call's lengths and tables: what
+// decode_auto_kernel computes before its first load (the piece bound, the
+// prefix of pieces, the clamped lengths, and for each wavefront its first
+// piece with the block ids of its first 64 blocks), stored once so that calls
+// which share lengths and tables (every layer of a decode step) start loading
+// keys at once.
 __global__ void __launch_bounds__(kWaves * 64)
 decode_plan_kernel(Params p) {
-  __shared__ int pfx[kAutoMaxBatch + 1];
+  __shared__ int pu[kAutoMaxBatch + 1];
   __shared__ int s_ctx[kAutoMaxBatch];
   __shared__ int wsum[kWaves];
+  __shared__ long long wtot[kWaves];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  block_prefix<false>(p, pfx, s_ctx, nullptr, wsum, tid, lane, wave);
-  const int64_t NB = (int64_t)p.Hkv * __builtin_amdgcn_readfirstlane(pfx[p.B]);
+  const int P = piece_prefix<false>(p, pu, s_ctx, nullptr, wsum, wtot, tid, lane, wave);
   const int W = gridDim.x * kWaves;
-  const int64_t G = NB / kRing;
-  const int64_t gbase = G / W;
-  const int64_t rem = G - gbase * W;
   if (blockIdx.x == 0) {
     for (int k = tid; k <= p.B; k += kWaves * 64) {
-      p.plan[kPlanHeaderInts + k] = pfx[k];
+      p.plan[kPlanHeaderInts + k] = pu[k];
       if (k < p.B) p.plan[kPlanCtxOffset + k] = s_ctx[k];
     }
     if (tid < kPlanHeaderInts) {
-      const int hdr[7] = {kPlanMagic, p.B, p.Hkv, p.max_blocks, p.ctx_cap, p.num_blocks, W};
-      p.plan[tid] = tid < 7 ? hdr[tid] : 0;
+      const int hdr[8] = {kPlanMagic, p.B, p.Hkv, p.max_blocks, p.ctx_cap, p.num_blocks, W, P};
+      p.plan[tid] = tid < 8 ? hdr[tid] : 0;
     }
   }
   const int w = blockIdx.x * kWaves + wave;
-  const int64_t x0 = share_start(w, gbase, rem);
-  const int64_t x1 = share_start(w + 1, gbase, rem);
   int* ent = p.plan + kPlanWaveOffset + (int64_t)w * kPlanWaveInts;
-  Cursor cc = {};
+  int f[8] = {-1, 0, 0, 0, 0, 1, 0, 0};
   int tab = 0;
-  if (x0 < x1) {
-    locate_share(cc, p, pfx, s_ctx, x0);
-    tab = id_window(p, s_ctx, cc, x0, x1, lane);
+  if ((int64_t)w < (int64_t)p.Hkv * pu_pieces(pu[p.B])) {
+    const Piece pc = locate_piece(p, pu, s_ctx, w);
+    f[0] = pc.b; f[1] = pc.g; f[2] = pc.j0; f[3] = pc.j1;
+    f[4] = pc.ctx; f[5] = pc.pieces; f[6] = pc.base; f[7] = pc.k;
+    if (pc.j1 > pc.j0) tab = piece_ids(p, pc, pc.j0, lane);
   }
-  ent[4 + lane] = tab;
-  if (lane < 4) ent[lane] = lane == 0 ? cc.b : lane == 1 ? cc.g : lane == 2 ? cc.j : cc.ctx;
+  ent[8 + lane] = tab;
+  if (lane < 8) {
+    int v = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v = lane == k ? f[k] : v;
+    ent[lane] = v;
+  }
 }
 
 //
 // kAppend: the call also stores one new token per sequence (kv_append with
 // one token each).  The new token is the last of its sequence, so it lies in
-// the stream's last block, which exactly one wavefront consumes: that
-// wavefront writes the token's K and V rows into the pools and uses them
-// from registers in place of the (stale) rows its load returned.  The rows
-// of a sequence clamped to max_context_len are stored by a workgroup during
+// the stream's last block, which exactly one piece reads: that wavefront
+// writes the token's K and V rows into the pools and uses them from
+// registers in place of the (stale) rows its load returned.  The rows of a
+// sequence clamped to max_context_len are stored by a workgroup during
 // set-up; slots outside the table or pool are not written (as kv_append).
 template <bool kAppend, bool kPlanned>
 __global__ void __launch_bounds__(kWaves * 64)
 decode_auto_kernel(Params p) {
   __shared__ float red[kWaves][8 * 4 * kD];
-  __shared__ int pfx[kAutoMaxBatch + 1];
+  __shared__ int pu[kAutoMaxBatch + 1];
   __shared__ int s_ctx[kAutoMaxBatch];
   __shared__ int wsum[kWaves];
+  __shared__ long long wtot[kWaves];
   __shared__ unsigned char s_newok[kAppend ? kAutoMaxBatch : 1];  // append this sequence
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gw = blockIdx.x * kWaves + wave;
+  const int W = gridDim.x * kWaves;
+  PieceRun r;
 
-  // per-sequence context lengths and the exclusive prefix of their padded
-  // block counts in LDS: read from the plan when one matches this call
-  const int grp = lane >> 3, i = lane & 7;
-  const bool quad1 = (i & 4) != 0;
-  const int c = quad1 ? ((i & 3) ^ 3) : (i & 3);
-  const int own_tok = quad1 ? grp + 8 : grp;
-  const int lane_off = grp * kD + 8 * i;
-  BlockRegs ring[kRing];
-  int nvalid[kRing];
-  int64_t ub[kRing];  // element offsets of the slots' blocks, for their V loads
-  bool slast[kRing];  // append: the slot holds its stream's last block
-  int sphys[kRing];   // append: that block's physical id
-  uint32_t qv[4][4], qn[4][4];
-  u32x4 knv, vnv, knn, vnn;  // append: new-token chunks (consumed / next group)
-  // Issue the first group of the share starting at stream position ci
-  // (id window tab, whose lane 0 is the group's first block).
-  auto prologue = [&](const Cursor& ci, int tab) {
-    load_q(qn, p, ci.b, ci.g, i, c);
-    if (kAppend) load_new(knn, vnn, p, ci.b, ci.g, i);
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) {
-      const int j = ci.j + s < ci.nbr - 1 ? ci.j + s : ci.nbr - 1;
-      const int id = __builtin_amdgcn_readlane(tab, s);
-      const int nv = issue_block(ring[s], p, id, ci.g, j, ci.ctx, lane_off);
-      nvalid[s] = ci.j + s < ci.nbr ? nv : 0;
-      if (kAppend) {
-        slast[s] = ci.j + s == ci.nbr - 1 && nv > 0;
-        sphys[s] = id;
-      }
-    }
-  };
-
-  // With a plan: its first group is issued at once, before the plan is
-  // checked against this call (the block ids are range-checked, so the loads
-  // stay inside the pools whatever the plan holds); the context lengths and
-  // the prefix come from the plan too.  A plan made for other lengths or
-  // another shape is not used: the split is computed and the first group
+  // With a plan: this wavefront's first piece is issued at once, before the
+  // plan is checked against this call (the block ids are range-checked, so
+  // the loads stay inside the pools whatever the plan holds); the lengths
+  // and the prefix come from the plan too.  A plan made for other lengths or
+  // another shape is not used: the split is computed and the first piece
   // issued again.
   bool use_plan = false, issued = false;
-  int pl_b = 0, pl_g = 0, pl_j = 0, pl_tab = 0;
+  Piece first = {};
   // this thread's first sequence (k = tid): plan prefix, plan length and
   // length, loaded before the first group so that waiting for them does not
   // wait for its keys (vector loads complete in order)
-  int v_pfx = 0, v_pctx = 0, v_len = 0;
+  int v_pu = 0, v_pctx = 0, v_len = 0;
   if (kPlanned) {
-    if (tid <= p.B) v_pfx = p.plan[kPlanHeaderInts + tid];
+    if (tid <= p.B) v_pu = p.plan[kPlanHeaderInts + tid];
     if (tid < p.B) {
       v_pctx = p.plan[kPlanCtxOffset + tid];
       v_len = p.context_lens[tid];
     }
     __builtin_amdgcn_sched_barrier(0);
-    const int w = blockIdx.x * kWaves + wave;
-    const int* ent = p.plan + kPlanWaveOffset + (int64_t)w * kPlanWaveInts;
-    pl_tab = ent[4 + lane];
-    pl_b = ld_uniform(ent, 0);
-    pl_g = ld_uniform(ent, 1);
-    pl_j = ld_uniform(ent, 2);
-    const int pl_ctx = ld_uniform(ent, 3);
+    const int* ent = p.plan + kPlanWaveOffset + (int64_t)gw * kPlanWaveInts;
+    const int tab = ent[8 + lane];
+    first.b = ld_uniform(ent, 0);
+    first.g = ld_uniform(ent, 1);
+    first.j0 = ld_uniform(ent, 2);
+    first.j1 = ld_uniform(ent, 3);
+    first.ctx = ld_uniform(ent, 4);
+    first.pieces = ld_uniform(ent, 5);
+    first.base = ld_uniform(ent, 6);
+    first.k = ld_uniform(ent, 7);
     use_plan = ld_uniform(p.plan, 0) == kPlanMagic && ld_uniform(p.plan, 1) == p.B &&
                ld_uniform(p.plan, 2) == p.Hkv && ld_uniform(p.plan, 3) == p.max_blocks &&
                ld_uniform(p.plan, 4) == p.ctx_cap && ld_uniform(p.plan, 5) == p.num_blocks &&
-               ld_uniform(p.plan, 6) == (int)(gridDim.x * kWaves);
-    if (use_plan && pl_ctx > 0 && pl_ctx <= p.ctx_cap && pl_b >= 0 && pl_b < p.B && pl_g >= 0 &&
-        pl_g < p.Hkv && pl_j >= 0) {
-      Cursor sc;
-      sc.b = pl_b;
-      sc.ctx = pl_ctx;
-      sc.nbr = (pl_ctx + kBS - 1) / kBS;
-      sc.nbp = (sc.nbr + kRing - 1) / kRing * kRing;
-      sc.g = pl_g;
-      sc.j = pl_j;
-      prologue(sc, pl_tab);
+               ld_uniform(p.plan, 6) == W;
+    if (use_plan && first.b >= 0 && first.b < p.B && first.g >= 0 && first.g < p.Hkv &&
+        first.ctx > 0 && first.ctx <= p.ctx_cap && first.j0 >= 0 && first.j0 < first.j1 &&
+        first.j1 <= (first.ctx + kBS - 1) / kBS && first.pieces >= 1 && first.k >= 0 &&
+        first.k < first.pieces) {
+      piece_begin<kAppend>(r, p, first, tab, lane);
       issued = true;
     }
   }
@@ -947,15 +1058,15 @@ decode_auto_kernel(Params p) {
     if (tid == 0) wsum[0] = 0;
     bool stale = false;
     for (int k = tid; k <= p.B; k += kWaves * 64) {
-      const bool first = k == tid;
-      pfx[k] = first ? v_pfx : p.plan[kPlanHeaderInts + k];
+      const bool own = k == tid;
+      pu[k] = own ? v_pu : p.plan[kPlanHeaderInts + k];
       if (k < p.B) {
-        int cx = first ? v_len : p.context_lens[k];
+        int cx = own ? v_len : p.context_lens[k];
         if (kAppend) s_newok[k] = cx >= 1 && cx <= p.ctx_cap;
         cx = cx < 0 ? 0 : (cx > p.ctx_cap ? p.ctx_cap : cx);  // as eff_ctx
         s_ctx[k] = cx;
         // the plan must have been made for exactly these lengths
-        stale = stale || (first ? v_pctx : p.plan[kPlanCtxOffset + k]) != cx;
+        stale = stale || (own ? v_pctx : p.plan[kPlanCtxOffset + k]) != cx;
       }
     }
     __syncthreads();
@@ -963,31 +1074,17 @@ decode_auto_kernel(Params p) {
     __syncthreads();
     if (wsum[0] != 0) {
       use_plan = false;
+      issued = false;
       __syncthreads();  // everyone has read the flag before wsum is reused
     }
   }
-  if (!use_plan) block_prefix<kAppend>(p, pfx, s_ctx, s_newok, wsum, tid, lane, wave);
+  if (!use_plan) piece_prefix<kAppend>(p, pu, s_ctx, s_newok, wsum, wtot, tid, lane, wave);
 
-  // ring groups are dealt out as evenly as possible: the first `rem`
-  // wavefronts take gbase + 1 groups, the others gbase
-  const int64_t NB = (int64_t)p.Hkv * __builtin_amdgcn_readfirstlane(pfx[p.B]);
-  const int W = gridDim.x * kWaves;
-  const int64_t G = NB / kRing;
-  const int64_t gbase = G / W;
-  const int64_t rem = G - gbase * W;
-  // empty sequences have no blocks, so no wavefront meets them: workgroup
-  // k % grid writes their zero rows
-  for (int k = blockIdx.x; k < p.B; k += gridDim.x) {
-    if (s_ctx[k] == 0) {
-      for (int e = tid; e < p.Hq * kD; e += kWaves * 64) {
-        const int64_t idx = (int64_t)k * p.Hq * kD + e;
-        if (p.out_f32) reinterpret_cast<float*>(p.out)[idx] = 0.f;
-        else reinterpret_cast<uint16_t*>(p.out)[idx] = 0;
-      }
-    }
-    // a sequence cut short by the clamp still gets its token stored (no
-    // wavefront reads that row): workgroup k % grid copies it
-    if (kAppend && !s_newok[k]) {
+  // a sequence cut short by the clamp still gets its token stored (no
+  // wavefront reads that row): workgroup k % grid copies it
+  if (kAppend) {
+    for (int k = blockIdx.x; k < p.B; k += gridDim.x) {
+      if (s_newok[k]) continue;
       const int len = p.context_lens[k];
       if (len >= 1 && len <= p.max_blocks * kBS) {
         const int pos = len - 1;
@@ -1005,196 +1102,33 @@ decode_auto_kernel(Params p) {
       }
     }
   }
-  const int w = blockIdx.x * kWaves + wave;
-  const int64_t x0 = share_start(w, gbase, rem);
-  const int64_t x1 = share_start(w + 1, gbase, rem);
-  if (x0 >= x1) return;
 
-  // locate x0 (or take it from the plan)
-  Cursor cc;
-  if (use_plan) {
-    cursor_load_seq(cc, s_ctx, pl_b);
-    cc.g = pl_g;
-    cc.j = pl_j;
-  } else {
-    locate_share(cc, p, pfx, s_ctx, x0);
+  // this wavefront's piece (already in flight with a plan)
+  if ((int64_t)gw >= (int64_t)p.Hkv * pu_pieces(__builtin_amdgcn_readfirstlane(pu[p.B]))) return;
+  Piece pc = first;
+  if (!issued) {
+    pc = locate_piece(p, pu, s_ctx, gw);
+    if (pc.j1 > pc.j0) piece_begin<kAppend>(r, p, pc, piece_ids(p, pc, pc.j0, lane), lane);
   }
-
-  // prologue: id window and q of the first group, then issue it
-  Cursor ci = cc;
-  int64_t xi = x0;
-  int64_t win = x0;
-  int tab = use_plan ? pl_tab : id_window(p, s_ctx, ci, x0, x1, lane);
-  if (!(use_plan && issued)) prologue(ci, tab);
-  if (xi + kRing < x1) {
-    xi += kRing;
-    cursor_advance(ci, s_ctx, p.Hkv, p.B);
-  } else {
-    xi = x1;  // nothing left to issue: further refills re-read this group
+  const int nb = (pc.ctx + kBS - 1) / kBS;
+  if (nb == 0) {
+    write_zero_rows(p, pc.b, pc.g, lane);
+    return;
   }
-  // refills re-read the last issued group once the share is used up
-  int64_t xr = xi < x1 ? xi : xi - kRing;
-  if (xr - win + kRing > 64) {
-    win = xr;
-    tab = id_window(p, s_ctx, ci, xr, x1, lane);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-  }
-
-  // pieces of split streams this share holds (at most its first and last)
-  int pend = 0, pb0 = 0, pg0 = 0, pb1 = 0, pg1 = 0;
-  RecordList prl0 = {}, prl1 = {};
-
+  const bool app = kAppend && pc.j1 == nb && s_newok[pc.b];
   LaneState st;
-  reset_state(st);
-  int64_t seg_start = x0;  // where the current segment began in this share
-  for (int64_t xc = x0; xc < x1; xc += kRing) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) qv[j][w2] = qn[j][w2];
-    if (kAppend) {
-      knv = knn;
-      vnv = vnn;
-      // the new token's row replaces the one loaded from the pools (its K
-      // here, its V before the slot's P.V), and is stored there (lanes
-      // grp == t % 8 hold token t in ka/va or kb/vb)
-#pragma unroll
-      for (int s = 0; s < kRing; ++s) {
-        if (slast[s] && s_newok[cc.b]) {
-          const int t = (cc.ctx - 1) & (kBS - 1);
-          if (grp == t) ring[s].ka = knv;
-          if (grp + 8 == t) ring[s].kb = knv;
-          if (grp == (t & 7)) {
-            const int64_t off = (((int64_t)sphys[s] * p.Hkv + cc.g) * kBS + t) * kD + 8 * i;
-            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.k_cache) + off) = knv;
-            *reinterpret_cast<u32x4*>(const_cast<uint16_t*>(p.v_cache) + off) = vnv;
-          }
-        }
-      }
-    }
-
-    bool full = true;
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) full = full && nvalid[s] == kBS;
-    float x[kRing];
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) {
-      x[s] = block_score(ring[s], qv, p.scale_log2, quad1);
-      if (!full && own_tok >= nvalid[s]) x[s] = -INFINITY;
-    }
-    // q, the new rows and the K halves of the group at ci go out now (a
-    // re-read when none is left), so they are in flight while this group is
-    // accumulated; each slot's V half follows its P.V
-    load_q(qn, p, ci.b, ci.g, i, c);
-    if (kAppend) load_new(knn, vnn, p, ci.b, ci.g, i);
-    int nv_next[kRing];
-    bool slast_next[kRing];
-    int sphys_next[kRing];
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) {
-      const int j = ci.j + s < ci.nbr - 1 ? ci.j + s : ci.nbr - 1;
-      const int id = __builtin_amdgcn_readlane(tab, (int)(xr - win) + s);
-      const int nv = issue_k(ring[s], p, id, ci.g, j, ci.ctx, lane_off, ub[s]);
-      nv_next[s] = ci.j + s < ci.nbr ? nv : 0;
-      if (kAppend) {
-        slast_next[s] = ci.j + s == ci.nbr - 1 && nv > 0;
-        sphys_next[s] = id;
-      }
-    }
-    float mx = x[0];
-#pragma unroll
-    for (int s = 1; s < kRing; ++s) mx = fmaxf(mx, x[s]);
-    mx = fmaxf(mx, dpp<kRowHalfMirror>(mx));
-    const float m_new = fmaxf(st.m, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
-    st.m = m_new;
-    st.l *= alpha;
-    const float a1 = dpp<kQuadXor1>(alpha), a2 = dpp<kQuadXor2>(alpha),
-                a3 = dpp<kQuadXor3>(alpha);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      st.acc[0][e] *= alpha;
-      st.acc[1][e] *= a1;
-      st.acc[2][e] *= a2;
-      st.acc[3][e] *= a3;
-    }
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) {
-      const float pw = __builtin_amdgcn_exp2f(x[s] - m_use);
-      st.l += pw;
-      if (kAppend && slast[s] && s_newok[cc.b]) {
-        const int t = (cc.ctx - 1) & (kBS - 1);
-        if (grp == t) ring[s].va = vnv;
-        if (grp + 8 == t) ring[s].vb = vnv;
-      }
-      if (full)
-        block_pv<false>(st, ring[s], pw, quad1, true, true);
-      else
-        block_pv<true>(st, ring[s], pw, quad1, grp < nvalid[s], grp + 8 < nvalid[s]);
-      issue_v(ring[s], p, ub[s], lane_off);
-      nvalid[s] = nv_next[s];
-      if (kAppend) {
-        slast[s] = slast_next[s];
-        sphys[s] = sphys_next[s];
-      }
-    }
-    if (xi + kRing < x1) {
-      xi += kRing;
-      cursor_advance(ci, s_ctx, p.Hkv, p.B);
-    } else {
-      xi = x1;
-    }
-    xr = xi < x1 ? xi : xi - kRing;
-    if (xr - win + kRing > 64) {
-      win = xr;
-      tab = id_window(p, s_ctx, ci, xr, x1, lane);
-      // wait here (vmcnt 0), inside the branch, so the common path carries
-      // no wait for this load
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-    }
-
-    // segment end: the stream ends here or the share does
-    const bool stream_ends = cc.j + kRing == cc.nbp;
-    if (stream_ends || xc + kRing >= x1) {
-      const int64_t stream_start =
-          (int64_t)p.Hkv * __builtin_amdgcn_readfirstlane(pfx[cc.b]) + (int64_t)cc.g * cc.nbp;
-      const bool complete = stream_ends && stream_start >= seg_start;
-      const int record = 2 * w + (stream_start <= x0 ? 0 : 1);
-      const int64_t w0 = share_of(stream_start, gbase, rem);
-      RecordList rl;
-      rl.base = 2 * w0;
-      rl.stride = 2;
-      rl.first_extra = stream_start > share_start(w0, gbase, rem) ? 1 : 0;
-      rl.pieces = (int)(share_of(stream_start + cc.nbp - 1, gbase, rem) - w0 + 1);
-      finish_segment(st, p, cc.b, cc.g, complete, record, rl, red[wave], lane);
-      if (!complete) {
-        if (pend == 0) {
-          pb0 = cc.b; pg0 = cc.g; prl0 = rl;
-        } else {
-          pb1 = cc.b; pg1 = cc.g; prl1 = rl;
-        }
-        ++pend;
-      }
-      reset_state(st);
-      seg_start = xc + kRing;
-    }
-    if (xc + kRing < x1) cursor_advance(cc, s_ctx, p.Hkv, p.B);
-  }
-  // count this share's split pieces only now: one drain instead of one per
-  // segment in the middle of the stream
-  if (pend) {
+  piece_run<kAppend>(st, r, p, pc, app, lane);
+  const bool complete = pc.pieces == 1;
+  RecordList rl;
+  rl.base = pc.base;
+  rl.stride = 1;
+  rl.first_extra = 0;
+  rl.pieces = pc.pieces;
+  finish_segment(st, p, pc.b, pc.g, complete, pc.base + pc.k, rl, red[wave], lane);
+  if (!complete) {
     drain_stores();
-    // both counts go out before either result is needed
-    const uint32_t c0 = count_piece(p, pb0, pg0, lane);
-    const uint32_t c1 = pend > 1 ? count_piece(p, pb1, pg1, lane) : 0u;
-    const bool m0 = c0 + 1 == (uint32_t)prl0.pieces;
-    const bool m1 = pend > 1 && c1 + 1 == (uint32_t)prl1.pieces;
-    if (m0 && m1) {  // both streams: their reads share one round trip
-      const MergeJob job[2] = {{pb0, pg0, prl0}, {pb1, pg1, prl1}};
-      merge_streams<2>(p, job, red[wave], lane);
-    } else if (m0 || m1) {
-      const MergeJob job[1] = {m0 ? MergeJob{pb0, pg0, prl0} : MergeJob{pb1, pg1, prl1}};
+    if (count_piece(p, pc.b, pc.g, lane) + 1 == (uint32_t)pc.pieces) {
+      const MergeJob job[1] = {{pc.b, pc.g, rl}};
       merge_streams<1>(p, job, red[wave], lane);
     }
   }
@@ -1243,7 +1177,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     const int grid = (int)((units + kWaves - 1) / kWaves);
     hipLaunchKernelGGL(decode_units_kernel<kFixed>, dim3(grid), dim3(kWaves * 64), 0, stream, p);
   } else {
-    const dim3 grid(kAutoWaves / kWaves), block(kWaves * 64);
+    const dim3 grid((unsigned)(auto_waves((int64_t)a.B * a.Hkv) / kWaves)), block(kWaves * 64);
     if (a.write_plan)
       hipLaunchKernelGGL(decode_plan_kernel, grid, block, 0, stream, p);
     else if (a.k_new && a.plan)

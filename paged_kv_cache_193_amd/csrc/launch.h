@@ -56,13 +56,19 @@ hipError_t launch_kv_append_rope(const RopeAppendArgs& a, hipStream_t stream);
 // Decode work decomposition (see decode.hip).
 enum DecodeMode : int { kWhole = 0, kFixed = 1, kAuto = 2 };
 
-// Fixed grid of wavefronts used by the balanced split: 8 per CU of a
-// 256-CU MI355X.  Part of the workspace-size formula, so a constant.
+// Wavefronts of the automatic split: 8 per CU of a 256-CU MI355X, or, for
+// more than 3/4 as many (sequence, KV head) streams, a quarter of that plus
+// one per stream (the split makes at most that many pieces, one per
+// wavefront), rounded up to whole workgroups of 4.
 #ifndef PKV_AUTO_WAVES
 #define PKV_AUTO_WAVES 2048
 #endif
 constexpr int kAutoWaves = PKV_AUTO_WAVES;
-// Largest batch the balanced split handles (per-sequence prefix in LDS).
+inline int64_t auto_waves(int64_t streams) {
+  const int64_t w = streams <= 3 * kAutoWaves / 4 ? kAutoWaves : kAutoWaves / 4 + streams;
+  return (w + 3) / 4 * 4;
+}
+// Largest batch the automatic split handles (per-sequence prefix in LDS).
 constexpr int kAutoMaxBatch = 4096;
 
 // One split record: normalised partial output for the 4 query heads of a
@@ -83,17 +89,19 @@ constexpr int kMaxRecords = (1 << 21) - 1;
 constexpr size_t kCounterBytes = (size_t)kMaxSplitStreams * kCounterStride * 4;
 
 // Decode plan (partition PKV_PARTITION_PLANNED), after the split records of
-// the balanced split: a header, the per-sequence prefix of padded block
-// counts, the (clamped) context lengths it was made for, and per wavefront
-// its first stream (b, g, j), that stream's length (0: no share) and the
-// block ids of its first 64 list positions.  Written by
-// paged_attention_decode_plan.
+// the automatic split: a header (with the piece bound), the per-sequence
+// prefix of pieces, the (clamped) context lengths it was made for, and per
+// wavefront its piece (b, g, first and end block, context length, the
+// stream's piece count and first record; b = -1: no piece) and the block ids
+// of its first 64 blocks.  Written by paged_attention_decode_plan.
 constexpr int kPlanHeaderInts = 16;
 constexpr int kPlanCtxOffset = kPlanHeaderInts + kAutoMaxBatch + 1;
 constexpr int kPlanWaveOffset = kPlanCtxOffset + kAutoMaxBatch;
-constexpr int kPlanWaveInts = 4 + 64;
+constexpr int kPlanWaveInts = 8 + 64;
 constexpr int kPlanMagic = 0x504c414e;
-constexpr size_t kPlanBytes = ((size_t)kPlanWaveOffset + (size_t)kAutoWaves * kPlanWaveInts) * 4;
+inline size_t plan_bytes(int64_t streams) {
+  return ((size_t)kPlanWaveOffset + (size_t)auto_waves(streams) * kPlanWaveInts) * 4;
+}
 
 struct DecodeArgs {
   void* out;

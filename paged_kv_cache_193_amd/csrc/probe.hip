@@ -8,7 +8,7 @@
 // chunks of both pools, 2 KB of K and 2 KB of V each at head_dim 64 and
 // block_size 16, for a list of physical block ids (those the block tables map
 // a batch's contexts to), with no arithmetic beyond folding the words into a
-// register.  The grid is the decode's balanced split grid (2048 wavefronts);
+// register.  The grid is the decode's automatic-split grid (2048 wavefronts);
 // each wavefront streams an equal contiguous share of the (block, head)
 // chunks, two chunks in flight, with 16-byte loads that cover whole
 // 128-byte rows.

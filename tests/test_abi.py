@@ -100,7 +100,10 @@ def test_decode_workspace_size(lib):
     rec = 4 * 64 + 8                              # floats per record
     counters = 32768 * 128                        # fixed counter region first: one per 128 B
     assert ws(4, 32, 64, 32768, 512) == counters + 4 * 8 * 64 * rec * 4
+    # automatic split: records only for streams cut into pieces, fewer than
+    # twice the 2048 wavefronts whatever the batch
     assert ws(64, 32, 64, 8192, -1) == counters + 2 * 2048 * rec * 4
+    assert ws(4096, 32, 64, 8192, -1) == counters + 2 * 2048 * rec * 4
     assert ws(4, 4, 64, 32768, 512) == counters + 4 * 1 * 64 * rec * 4   # one KV head
     assert ws(4097, 32, 64, 8192, 512) == 0       # too many streams -> rejected
     assert ws(8, 32, 128, 2048, 512) == 0         # rejected -> 0
@@ -173,8 +176,12 @@ def test_planned_workspace_holds_the_plan(lib):
     ws = pkv.paged_attention_decode_workspace_size
     auto = ws(64, 32, 64, 8192, pkv.PARTITION_AUTO)
     planned = ws(64, 32, 64, 8192, pkv.PARTITION_PLANNED)
-    plan_ints = 16 + 4097 + 4096 + 2048 * 68
+    plan_ints = 16 + 4097 + 4096 + 2048 * 72   # header, prefix, lengths, 2048 entries
     assert planned == (auto + 255) // 256 * 256 + plan_ints * 4
+    # more than 1536 (sequence, KV head) streams: 512 + one wavefront per stream
+    auto = ws(256, 32, 64, 8192, pkv.PARTITION_AUTO)
+    plan_ints = 16 + 4097 + 4096 + (512 + 256 * 8) * 72
+    assert ws(256, 32, 64, 8192, pkv.PARTITION_PLANNED) == (auto + 255) // 256 * 256 + plan_ints * 4
     assert decode_call(lib, part=pkv.PARTITION_PLANNED) == pkv.PKV_ERR_WORKSPACE
     assert plan_call(lib, B=0, bt=None, cl=None) == pkv.PKV_OK
 

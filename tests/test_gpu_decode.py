@@ -2,7 +2,7 @@
 
 Bar: max-abs <= 1e-2 and mean-abs <= 1e-3 against the fp64 oracle (fp32
 output); bf16 output within max(1e-2, 1 bf16 ulp) of the oracle rounded to
-bf16.  Every split mode (none, fixed partitions, automatic balanced split) is
+bf16.  Every split mode (none, fixed partitions, automatic stream-aligned split) is
 checked on every case.
 """
 import numpy as np
@@ -169,7 +169,7 @@ def test_long_context_split_full_size():
     assert_close(got.cpu().numpy(), ref, "long 512")
     auto = gpu_decode(c, pkv.PARTITION_AUTO, k=c.extra["k_layers"][0], v=c.extra["v_layers"][0])
     assert_close(auto.cpu().numpy(), ref, "long auto")
-    # with the balanced split's plan (as the benchmark times it): the same bits
+    # with the automatic split's plan (as the benchmark times it): the same bits
     k, v = c.extra["k_layers"][0], c.extra["v_layers"][0]
     t, l = dev(c.block_tables), dev(c.context_lens)
     ws = pkv.decode_workspace(c.B, c.Hq, c.D, c.max_context_len,
