@@ -641,10 +641,13 @@ decode_units_kernel(Params p) {
 // kAuto: stream-aligned pieces, one per wavefront.
 //
 // The batch's blocks are cut into pieces, each inside one stream (sequence b,
-// KV head g).  A piece holds at most P blocks, the smallest bound that leaves
-// one wavefront per stream spare,
-//     P = max(kMinPiece, ceil(NB * Hkv / max(W - S, W / 4))),
-// for NB blocks over the sequences, S = B * Hkv streams and W = kAutoWaves.  A
+// KV head g).  A piece holds at most P blocks: the smallest bound (at least
+// kMinPiece) whose pieces fit the grid of W = kAutoWaves wavefronts, found by
+// a short search between ceil(NB * Hkv / W) and the bound that leaves one
+// wavefront per stream spare,
+//     max(kMinPiece, ceil(NB * Hkv / max(W - S, W / 4))),
+// for NB blocks over the sequences and S = B * Hkv streams (that bound alone
+// when there are more than 3W/4 streams and the grid grows).  A
 // stream of nb blocks is cut into u = ceil(nb / P) pieces of equal length
 // (piece k: blocks [k nb / u, (k + 1) nb / u)); an empty stream is one piece
 // that writes zero rows.  That makes at most W pieces when S <= 3W/4 and at
@@ -733,7 +736,32 @@ __device__ __forceinline__ int piece_prefix(const Params& p, int* pu, int* s_ctx
   __syncthreads();
   long long tot = 0;
   for (int w2 = 0; w2 < kWaves; ++w2) tot += wtot[w2];
-  const int P = piece_bound(tot, p.B, p.Hkv, kAutoWaves);
+  // the smallest bound whose pieces still fit the grid: piece counts only
+  // fall as the bound grows, and piece_bound's value fits.  Searched on the
+  // fixed grid only (there records <= pieces <= W; a grid grown for many
+  // streams keeps piece_bound's value, whose cut pieces stay below W / 2).
+  // Every wavefront searches on its own over the lengths in LDS, so the
+  // search needs no barrier.
+  const int64_t grid_waves = (int64_t)gridDim.x * kWaves;
+  int hi = piece_bound(tot, p.B, p.Hkv, kAutoWaves);
+  // no bound below ceil(NB * Hkv / W) fits: the search starts there
+  const long long floor_p = (tot * p.Hkv + grid_waves - 1) / grid_waves;
+  int lo = grid_waves == kAutoWaves
+               ? (int)(floor_p > kMinPiece ? (floor_p < hi ? floor_p : hi) : kMinPiece) - 1
+               : hi;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    // per-lane counts clamped at 2^17, so the wave's float sum (DPP rows,
+    // then readlane) is exact wherever the comparison is close
+    int n = 0;
+    for (int k = lane; k < p.B; k += 64) {
+      n += pieces_of((s_ctx[k] + kBS - 1) / kBS, mid);
+      n = n < (1 << 17) ? n : (1 << 17);
+    }
+    const float all = wave_sum_u((float)n);
+    if ((double)all * p.Hkv <= (double)grid_waves) hi = mid; else lo = mid;
+  }
+  const int P = hi;
   int local = 0;
   for (int k = beg; k < end; ++k) local += prefix_word((s_ctx[k] + kBS - 1) / kBS, P);
   int incl = local;
