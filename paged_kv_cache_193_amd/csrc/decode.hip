@@ -213,123 +213,6 @@ __device__ __forceinline__ void block_pv(LaneState& st, const BlockRegs& r, floa
     for (int e = 0; e < 8; ++e) st.acc[j][e] = dot2_bf16(ps[j], v2[e], st.acc[j][e]);
 }
 
-// Run blocks [j0, j1) of stream (b, g) through one wavefront.
-//
-// The blocks go through a ring of kRing register slots in groups of kRing:
-// the scores of a whole group are formed first, the running max moves once
-// per group (one rescale of the accumulator, no branch), then P.V runs block
-// by block.  Each slot is refilled with the block kRing ahead in two halves:
-// its K as soon as the group's scores are formed, its V as soon as its own
-// P.V is done, so the next group's loads are in flight while this group is
-// scored and while it is accumulated.  Every group issues exactly kRing
-// block loads (past the segment end the last block is re-read, a cache hit
-// marked invalid), so the hardware wait counts stay exact.
-__device__ __forceinline__ void run_segment(LaneState& st, const Params& p, int b, int g,
-                                            int j0, int j1, int ctx, int lane) {
-  const int grp = lane >> 3, i = lane & 7;
-  const bool quad1 = (i & 4) != 0;
-  const int c = quad1 ? ((i & 3) ^ 3) : (i & 3);
-  const int own_tok = quad1 ? grp + 8 : grp;
-
-  // this lane's query chunks, head order slot j -> head j ^ c
-  uint32_t qv[4][4];
-  const uint16_t* qb = p.q + ((int64_t)b * p.Hq + 4 * g) * kD + 8 * i;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    u32x4 v = *reinterpret_cast<const u32x4*>(qb + (j ^ c) * kD);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) qv[j][w] = v[w];
-  }
-
-  st.m = -INFINITY;
-  st.l = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) st.acc[j][e] = 0.f;
-
-  const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks;
-  const int lane_off = grp * kD + 8 * i;
-  const int nb = j1 - j0;
-  const int last = j1 - 1;
-  // block ids: lane k of `tab` holds the id of block tab_base + k (clamped to
-  // the segment), read with readlane; refilled once per 64 blocks
-  int tab_base = j0;
-  int tab = trow[j0 + lane < last ? j0 + lane : last];
-
-  BlockRegs ring[kRing];
-  int nvalid[kRing];
-  int64_t ub[kRing];  // element offsets of the slots' blocks, for their V loads
-#pragma unroll
-  for (int s = 0; s < kRing; ++s) {
-    const int j = j0 + s < last ? j0 + s : last;
-    const int nv = issue_block(ring[s], p, __builtin_amdgcn_readlane(tab, j - tab_base), g, j,
-                               ctx, lane_off);
-    nvalid[s] = s < nb ? nv : 0;
-  }
-
-  for (int base = 0; base < nb; base += kRing) {
-    bool full = true;
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) full = full && nvalid[s] == kBS;
-    float x[kRing];
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) {
-      x[s] = block_score(ring[s], qv, p.scale_log2, quad1);
-      if (!full && own_tok >= nvalid[s]) x[s] = -INFINITY;
-    }
-    // the K halves of the slots are free: refill them with the blocks kRing
-    // ahead (their V halves follow each slot's P.V)
-    int nv_next[kRing];
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) {
-      const int jn = j0 + base + s + kRing;
-      const int j = jn < last ? jn : last;
-      if (j - tab_base >= 64) {
-        tab_base += 64;
-        tab = trow[tab_base + lane < last ? tab_base + lane : last];
-        // wait here (vmcnt 0), inside the branch, so the common path after it
-        // carries no wait for this load
-        __builtin_amdgcn_s_waitcnt(0x0F70);
-      }
-      const int nv = issue_k(ring[s], p, __builtin_amdgcn_readlane(tab, j - tab_base), g, j, ctx,
-                             lane_off, ub[s]);
-      nv_next[s] = jn < j1 ? nv : 0;
-    }
-    // one max per group, shared by the mirror pair (same head, tokens t, t+8)
-    float mx = x[0];
-#pragma unroll
-    for (int s = 1; s < kRing; ++s) mx = fmaxf(mx, x[s]);
-    mx = fmaxf(mx, dpp<kRowHalfMirror>(mx));
-    const float m_new = fmaxf(st.m, mx);
-    // no valid token yet on this lane pair: keep everything at zero weight
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
-    st.m = m_new;
-    st.l *= alpha;
-    const float a1 = dpp<kQuadXor1>(alpha), a2 = dpp<kQuadXor2>(alpha),
-                a3 = dpp<kQuadXor3>(alpha);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      st.acc[0][e] *= alpha;
-      st.acc[1][e] *= a1;
-      st.acc[2][e] *= a2;
-      st.acc[3][e] *= a3;
-    }
-#pragma unroll
-    for (int s = 0; s < kRing; ++s) {
-      const float pw = __builtin_amdgcn_exp2f(x[s] - m_use);  // 0 for x = -inf
-      st.l += pw;
-      if (full)
-        block_pv<false>(st, ring[s], pw, quad1, true, true);
-      else
-        block_pv<true>(st, ring[s], pw, quad1, grp < nvalid[s], grp + 8 < nvalid[s]);
-      issue_v(ring[s], p, ub[s], lane_off);
-      nvalid[s] = nv_next[s];
-    }
-  }
-}
-
 // Combine the 64 lanes' states of a finished segment and write either the
 // final rows out[b][4g..4g+3][:] or a split record.  red: this wave's 8 KB.
 __device__ __forceinline__ void finish_segment(const LaneState& st, const Params& p, int b,
@@ -593,50 +476,6 @@ __device__ __forceinline__ void write_zero_rows(const Params& p, int b, int g, i
     *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + row) = u32x2{0, 0};
 }
 
-// kWhole / kFixed: one wavefront per (b, g, partition) unit.
-template <int kMode>
-__global__ void __launch_bounds__(kWaves * 64)
-decode_units_kernel(Params p) {
-  __shared__ float red[kWaves][8 * 4 * kD];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int unit = blockIdx.x * kWaves + wave;
-  const int parts = (kMode == kWhole) ? 1 : p.parts_max;
-  const int stream = unit / parts;
-  const int part = unit - stream * parts;
-  if (stream >= p.B * p.Hkv) return;
-  const int b = stream / p.Hkv;
-  const int g = stream - b * p.Hkv;
-  const int ctx = eff_ctx(p, b);
-  const int nb = (ctx + kBS - 1) / kBS;
-  if (nb == 0) {
-    if (part == 0) write_zero_rows(p, b, g, lane);
-    return;
-  }
-  int j0 = 0, j1 = nb;
-  if (kMode == kFixed) {
-    j0 = part * p.part_blocks;
-    if (j0 >= nb) return;
-    j1 = j0 + p.part_blocks < nb ? j0 + p.part_blocks : nb;
-  }
-  LaneState st;
-  run_segment(st, p, b, g, j0, j1, ctx, lane);
-  const bool complete = (j0 == 0 && j1 == nb);
-  RecordList rl;
-  rl.base = (int64_t)stream * parts;
-  rl.stride = 1;
-  rl.first_extra = 0;
-  rl.pieces = (nb + p.part_blocks - 1) / (p.part_blocks > 0 ? p.part_blocks : 1);
-  finish_segment(st, p, b, g, complete, unit, rl, red[wave], lane);
-  if (!complete) {
-    drain_stores();
-    if (count_piece(p, b, g, lane) + 1 == (uint32_t)rl.pieces) {
-      const MergeJob job[1] = {{b, g, rl}};
-      merge_streams<1>(p, job, red[wave], lane);
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
 // kAuto: stream-aligned pieces, one per wavefront.
 //
@@ -868,7 +707,7 @@ __device__ __forceinline__ void piece_begin(PieceRun& r, const Params& p, const 
   }
 }
 
-// Run the piece's blocks through its ring (as run_segment); with `app` the
+// Run the piece's blocks through its ring; with `app` the
 // new token's rows replace the stale ones its last block returned and are
 // stored to the pools.
 template <bool kAppend>
@@ -966,6 +805,58 @@ __device__ __forceinline__ void piece_run(LaneState& st, PieceRun& r, const Para
       issue_v(r.ring[s], p, r.ub[s], lane_off);
       r.nvalid[s] = nv_next[s];
       if (kAppend) r.slast[s] = sl_next[s];
+    }
+  }
+}
+
+// kWhole / kFixed: one wavefront per (b, g, partition) unit.
+template <int kMode>
+__global__ void __launch_bounds__(kWaves * 64)
+decode_units_kernel(Params p) {
+  __shared__ float red[kWaves][8 * 4 * kD];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int unit = blockIdx.x * kWaves + wave;
+  const int parts = (kMode == kWhole) ? 1 : p.parts_max;
+  const int stream = unit / parts;
+  const int part = unit - stream * parts;
+  if (stream >= p.B * p.Hkv) return;
+  const int b = stream / p.Hkv;
+  const int g = stream - b * p.Hkv;
+  const int ctx = eff_ctx(p, b);
+  const int nb = (ctx + kBS - 1) / kBS;
+  if (nb == 0) {
+    if (part == 0) write_zero_rows(p, b, g, lane);
+    return;
+  }
+  int j0 = 0, j1 = nb;
+  if (kMode == kFixed) {
+    j0 = part * p.part_blocks;
+    if (j0 >= nb) return;
+    j1 = j0 + p.part_blocks < nb ? j0 + p.part_blocks : nb;
+  }
+  Piece pc = {};
+  pc.b = b;
+  pc.g = g;
+  pc.j0 = j0;
+  pc.j1 = j1;
+  pc.ctx = ctx;
+  PieceRun r;
+  piece_begin<false>(r, p, pc, piece_ids(p, pc, j0, lane), lane);
+  LaneState st;
+  piece_run<false>(st, r, p, pc, false, lane);
+  const bool complete = (j0 == 0 && j1 == nb);
+  RecordList rl;
+  rl.base = (int64_t)stream * parts;
+  rl.stride = 1;
+  rl.first_extra = 0;
+  rl.pieces = (nb + p.part_blocks - 1) / (p.part_blocks > 0 ? p.part_blocks : 1);
+  finish_segment(st, p, b, g, complete, unit, rl, red[wave], lane);
+  if (!complete) {
+    drain_stores();
+    if (count_piece(p, b, g, lane) + 1 == (uint32_t)rl.pieces) {
+      const MergeJob job[1] = {{b, g, rl}};
+      merge_streams<1>(p, job, red[wave], lane);
     }
   }
 }
