@@ -205,6 +205,48 @@ def test_shared_workspace_reused_across_calls(partition):
             assert int(counters.abs().sum()) == 0
 
 
+def test_many_streams_with_cut_contexts():
+    """256 sequences (2048 (sequence, KV head) streams, more than the 1536 up
+    to which the automatic split keeps its fixed 2048-wavefront grid: the grid
+    grows to 512 + one wavefront per stream and the piece bound leaves one
+    wavefront per stream spare) with contexts log-uniform in [16, 4096], so
+    long streams are cut and merged: automatic, planned and append forms
+    against the oracle on every row, counters left at zero."""
+    B, maxb = 256, 256
+    g = wl.generator(67)
+    lens = wl.draw_lens(g, B, ("loguniform", 16, 4096))
+    N = int(wl.blocks_needed(lens, 16).sum()) + 1
+    tables = wl.tables_from_permutation(g, lens, 16, N, maxb, filler=N - 1)
+    q = wl.randn_bf16(g, (B, 32, 64))
+    k_cache, v_cache = wl.randn_bf16(g, (N, 8, 16, 64)), wl.randn_bf16(g, (N, 8, 16, 64))
+    ref = oracle.decode(u16(q), u16(k_cache), u16(v_cache), tables.numpy(), lens.numpy(), 0.125,
+                        threads=8)
+    k, v, qd, t, l = dev(k_cache), dev(v_cache), dev(q), dev(tables), dev(lens)
+    mx = int(lens.max())
+    for mode in (pkv.PARTITION_AUTO, pkv.PARTITION_PLANNED):
+        ws = pkv.decode_workspace(B, 32, 64, mx, mode, "cuda")
+        if mode == pkv.PARTITION_PLANNED:
+            pkv.paged_attention_decode_plan(k, t, l, 32, mx, ws)
+        out = torch.full((B, 32, 64), float("nan"), dtype=torch.float32, device="cuda")
+        pkv.paged_attention_decode(out, qd, k, v, t, l, 0.125, mx, mode, ws)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), ref, f"B=256 cut streams mode={mode}")
+        assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
+    # the append form on the same split, storing each sequence's last token
+    # again: the pools stay as they were and the output is the same
+    last = (lens - 1).clamp(min=0)
+    blk = tables[torch.arange(B), (last // 16).long()].long()
+    kn = k_cache[blk, :, (last % 16).long()].contiguous()
+    vn = v_cache[blk, :, (last % 16).long()].contiguous()
+    ws = pkv.decode_workspace(B, 32, 64, mx, pkv.PARTITION_AUTO, "cuda")
+    out = torch.full((B, 32, 64), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_attention_decode_append(out, qd, k, v, dev(kn), dev(vn), t, l, 0.125, mx,
+                                      pkv.PARTITION_AUTO, ws)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, f"B=256 cut streams append")
+    assert torch.equal(k.cpu(), k_cache) and torch.equal(v.cpu(), v_cache)
+
+
 def test_largest_batch_of_the_automatic_split():
     """B = 4096 sequences (32768 streams, the automatic split's limit) with
     short ragged contexts, some empty: automatic and planned splits against
