@@ -464,13 +464,19 @@ PKV_API int paged_attention_decode_append(void *out, int32_t out_dtype, const vo
  * q             [T_q][Hq][D] bf16, packed by sequence.
  * cu_q_lens     [B+1] int32 prefix sums of query tokens per sequence.
  * max_q_len     host-side upper bound of the per-sequence query counts
- *               (values above T_q are taken as T_q).  Query tiles are
- *               launched for the first max_q_len rows of each sequence
- *               only: rows past them in a longer sequence are not written.
+ *               (values above T_q are taken as T_q).  Only the first
+ *               max_q_len rows of each sequence are computed and written:
+ *               rows past them in a longer sequence keep what out held.
  * Other arguments as for decode.  This build implements D == 64,
- * block_size == 16 and Hq == 4 * Hkv.  One workgroup of 256 threads runs per
- * 32-row query tile of max_q_len, sequence and KV head; a grid beyond one
- * launch (2^32 - 1 work-items) returns PKV_ERR_UNSUPPORTED.
+ * block_size == 16 and Hq == 4 * Hkv.  Workgroups of 256 threads: one per
+ * 32-row query tile, sequence and KV head; a sequence of at most 4 query
+ * rows (a decoding sequence of a mixed batch, a few draft tokens) is one
+ * workgroup per KV head whose 4 wavefronts split its context.  The grid has
+ * ceil(min(max_q_len, T_q) / 32) ranks per sequence, or, for at most 256
+ * sequences where at most 1/8 of those would hold a query tile, only
+ * B + T_q / 32 units per KV head (the tiles of a rank found on the device);
+ * a grid beyond one launch (2^32 - 1 work-items) returns
+ * PKV_ERR_UNSUPPORTED.
  */
 PKV_API int paged_attention_prefill_causal(void *out, int32_t out_dtype, const void *q,
                                    const void *k_cache, const void *v_cache,

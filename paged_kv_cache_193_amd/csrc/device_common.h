@@ -38,6 +38,7 @@ enum : int {
   kQuadXor2 = 0x4E,        // quad_perm [2,3,0,1]
   kQuadXor3 = 0x1B,        // quad_perm [3,2,1,0]
   kRowHalfMirror = 0x141,  // lane i <-> 7-i inside each group of 8
+  kRowMirror = 0x140,      // lane i <-> 15-i inside each row of 16
   kRowRor8 = 0x128,        // lane i <- lane (i+8) mod 16 inside each row of 16
   kRowRor4 = 0x124,        // rotations of a row of 16 by 4, 2, 1 lanes
   kRowRor2 = 0x122,

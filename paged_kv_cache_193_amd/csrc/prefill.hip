@@ -13,8 +13,10 @@
 //   O^T[64 d][32 q]     += V^T . P^T     (2 MFMA tiles of 32x32)
 // 32-row query tiles halve the longest unit of work (the last rows of a long
 // prompt see every key tile) and leave room for three workgroups per CU
-// (133 VGPRs, 36 KB of LDS); a one-token row of a mixed batch wastes 31 rows
-// of a tile instead of 63.
+// (142 VGPRs, 36 KB of LDS).  A sequence of at most 4 query rows (a decoding
+// sequence of a mixed batch) takes its own path, short_rows below: its
+// workgroup's 4 wavefronts split the context instead of walking all of it
+// with a 32-row tile that holds one row.
 // The MFMA accumulator layout puts one query column and 16 keys in a lane
 // (rows 8*(r/4) + 4*(lane/32) + r%4, column lane%32), which is exactly the
 // layout P^T needs as the B operand of the next product: the softmax runs on
@@ -78,6 +80,8 @@ struct PParams {
   const int32_t* context_lens;
   const int32_t* cu_q_lens;
   int B, Hq, Hkv, max_blocks, num_blocks, tiles_max;
+  int max_rows;     // rows of a sequence that are written: min(max_q_len, T_q)
+  int chunks;       // compact grid: ceil(B / 64) sequences per lane; 0: rank grid
   float c_log2;     // |scale| * log2(e), floored at 1e-30: scores to log2 units
   uint32_t q_sign;  // 0x80008000 when scale < 0 (q is negated), else 0
 };
@@ -166,10 +170,345 @@ __device__ __forceinline__ u32x2 v_keys4(const uint16_t* vs, int key0, int d0, i
   return __builtin_bit_cast(u32x2, x);
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Short rows: a sequence with at most kShortRows query rows (a decoding
+// sequence of a mixed batch, or a few draft tokens) has one live workgroup
+// and little to contract, but its context can be long.  Its 4 wavefronts
+// split the context's blocks into 4 contiguous ranges, and each wavefront
+// covers all 4 heads of the group for every row at once: the 16 columns of
+// a 16x16x32 MFMA are (row t, head) = (c / 4, c % 4).  Per wavefront and
+// 64-key group (4 blocks):
+//   S^T[16 keys][16 cols] = K . Q^T        4 blocks x 2 head_dim halves
+//   O^T[16 d][16 cols]   += V^T . P^T      4 head_dim quarters x 2 key halves
+// The K operand (key l % 16, head_dim chunk l / 16 of one half) is one
+// 16-byte load per lane straight from the block; V goes through the
+// wavefront's own quarter of the LDS (row major) and is read transposed.
+// The 16x16 accumulator gives lane l keys 4 * (l / 16) + i (i < 4) of
+// column l % 16; the P^T operand of a 32-key half takes them from its two
+// blocks, and the V^T operand reads the same keys (4 from each block).  The
+// softmax takes the exact maximum of every group.  The four wavefronts'
+// (max, sum, O^T) are combined by the log-sum-exp rule through LDS.
+constexpr int kShortRows = 4;
+
+__device__ __forceinline__ void short_rows(const PParams& p, uint16_t* lds, int b, int g,
+                                           int qs, int q_len, int ctx, int tid) {
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15;   // column: row n / 4, head 4 * g + n % 4
+  const int j = lane >> 4;   // k group of the MFMA operands
+  const int t = n >> 2;
+  const int hist = ctx - q_len;
+  const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks;
+  const float c2 = p.c_log2;
+
+  // Q^T operand: column n, head_dim [32 s + 8 j, +8) for s = 0, 1 (zero for
+  // columns past the rows; their results are not written)
+  u32x4 qv[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+  if (t < q_len) {
+    const uint16_t* qr = p.q + ((int64_t)(qs + t) * p.Hq + 4 * g + (n & 3)) * kD + 8 * j;
+    const u32x4 sg = {p.q_sign, p.q_sign, p.q_sign, p.q_sign};
+    qv[0] = *reinterpret_cast<const u32x4*>(qr) ^ sg;
+    qv[1] = *reinterpret_cast<const u32x4*>(qr + 32) ^ sg;
+  }
+  // keys this column sees: 0 .. min(position, ctx - 1)
+  const int lim_col = hist + t < ctx - 1 ? hist + t : ctx - 1;
+
+  // this wavefront's blocks [bw0, bw1) and keys [16 * bw0, wend)
+  const int nblk = ctx > 0 ? (ctx + kBS - 1) / kBS : 0;
+  const int bw0 = wave * nblk / 4, bw1 = (wave + 1) * nblk / 4;
+  const int wend = 16 * bw1 < ctx ? 16 * bw1 : ctx;
+  const int n_groups = (bw1 - bw0 + 3) / 4;
+  uint16_t* vs = lds + wave * (kTile * kKRow);
+
+  float m_ref = -INFINITY;  // column maximum so far (log2 units)
+  float l_run = 0.f;        // this lane's share of the column sum
+  f32x4 o[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
+                {0.f, 0.f, 0.f, 0.f}};  // O^T rows 16 dt + 4 j + i, column n
+
+  if (n_groups > 0) {
+    // lane offsets (bytes) inside a (block, head) chunk of 16 x 64 bf16
+    const uint32_t koff = (uint32_t)((lane & 15) * 128 + 16 * j);  // + 64 s
+    const uint32_t voff = (uint32_t)(16 * lane);                     // + 1024
+    // block ids of a group; blocks past the range repeat the range's last
+    // block (the loads stay unconditional and hit the cache)
+    auto ids = [&](int jb0, int* id) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int jb = jb0 + jj < bw1 ? jb0 + jj : bw1 - 1;
+        id[jj] = trow[__builtin_amdgcn_readfirstlane(jb)];
+      }
+    };
+    auto rsrc = [&](const uint16_t* pool, int phys) {
+      phys = __builtin_amdgcn_readfirstlane(phys);
+      phys = phys >= 0 && phys < p.num_blocks ? phys : 0;
+      return __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(pool + ((int64_t)phys * p.Hkv + g) * (kBS * kD)), (short)0,
+          kBS * kD * 2, kRsrcWord3);
+    };
+    u32x4 kr[4][2], vr[4][2];
+    auto load_k = [&](const int* id) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const __amdgpu_buffer_rsrc_t r = rsrc(p.k_cache, id[jj]);
+        kr[jj][0] = __builtin_amdgcn_raw_buffer_load_b128(r, koff, 0, 0);
+        kr[jj][1] = __builtin_amdgcn_raw_buffer_load_b128(r, koff + 64, 0, 0);
+      }
+    };
+    auto load_v = [&](const int* id) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const __amdgpu_buffer_rsrc_t r = rsrc(p.v_cache, id[jj]);
+        vr[jj][0] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+        vr[jj][1] = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 1024, 0, 0);
+      }
+    };
+    int id[4];
+    ids(bw0, id);
+    load_k(id);
+    load_v(id);
+    ids(bw0 + 4, id);
+
+    for (int gi = 0; gi < n_groups; ++gi) {
+      const int k0 = 16 * (bw0 + 4 * gi);
+      // V of this group into the wavefront's LDS quarter; rows of keys past
+      // the range are zeroed (0 * NaN must not reach the MFMA)
+      if (k0 + kTile > wend) {
+        const u32x4 zero = {0, 0, 0, 0};
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          if (k0 + 16 * jj + (lane >> 3) >= wend) vr[jj][0] = zero;
+          if (k0 + 16 * jj + 8 + (lane >> 3) >= wend) vr[jj][1] = zero;
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        *reinterpret_cast<u32x4*>(vs + (16 * jj + (lane >> 3)) * kKRow + 8 * (lane & 7)) =
+            vr[jj][0];
+        *reinterpret_cast<u32x4*>(vs + (16 * jj + 8 + (lane >> 3)) * kKRow + 8 * (lane & 7)) =
+            vr[jj][1];
+      }
+      load_v(id);
+
+      // S^T = K . Q^T, one 16-key block per accumulator
+      f32x4 s[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        s[jj] = mfma16(as_bf16x8(kr[jj][0]), as_bf16x8(qv[0]), f32x4{0.f, 0.f, 0.f, 0.f});
+        s[jj] = mfma16(as_bf16x8(kr[jj][1]), as_bf16x8(qv[1]), s[jj]);
+      }
+      load_k(id);
+      ids(bw0 + 4 * gi + 8, id);
+
+      // mask keys past the column's position or the range
+      const int lim_row0 = (hist < ctx - 1 ? hist : ctx - 1);
+      if (k0 + kTile - 1 > (lim_row0 < wend - 1 ? lim_row0 : wend - 1)) {
+        const int lim = (lim_col < wend - 1 ? lim_col : wend - 1) - (k0 + 4 * j);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (16 * jj + i > lim) s[jj][i] = -INFINITY;
+      }
+
+      // exact column maximum of the group, rescale, weights
+      float v = fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3]));
+#pragma unroll
+      for (int jj = 1; jj < 4; ++jj)
+        v = fmaxf(v, fmaxf(fmaxf(s[jj][0], s[jj][1]), fmaxf(s[jj][2], s[jj][3])));
+      v = fmaxf(v, shfl_xor(v, 16));
+      v = fmaxf(v, shfl_xor(v, 32));
+      const float m_new = fmaxf(m_ref, v * c2);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_use);  // 0 while no reference
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+      m_ref = m_new;
+      bf16x8_t pop[2];
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps) {
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x4& sv = s[2 * ps + (e >> 1)];
+          const int i = 2 * (e & 1);
+          w[e] = pack_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], c2, -m_use)),
+                           __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i + 1], c2, -m_use)));
+          l_run = dot2_bf16(w[e], kOnesBf16x2, l_run);
+        }
+        pop[ps] = as_bf16x8(w);
+      }
+
+      // O^T += V^T . P^T: keys 32 ps + 4 j + (0..3) and 32 ps + 16 + 4 j + (0..3)
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const u32x2 lo = v_keys4(vs, 32 * ps + 4 * j, 16 * dt, lane);
+          const u32x2 hi = v_keys4(vs, 32 * ps + 16 + 4 * j, 16 * dt, lane);
+          o[dt] = mfma16(as_bf16x8(u32x4{lo[0], lo[1], hi[0], hi[1]}), pop[ps], o[dt]);
+        }
+    }
+  }
+
+  // combine the four wavefronts: each writes (max, sum, O^T) of its 16
+  // columns to its LDS quarter, then every thread finishes 4 outputs
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+  float* part = reinterpret_cast<float*>(vs);  // [16] max, [16] sum, [16][64] O
+  if (j == 0) {
+    part[n] = m_ref;
+    part[16 + n] = l_run;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    *reinterpret_cast<f32x4*>(part + 32 + n * kD + 16 * dt + 4 * j) = o[dt];
+  __syncthreads();
+
+  const int col = tid >> 4, d = 4 * (tid & 15);
+  const int row = col >> 2;
+  const int wr_len = q_len < p.max_rows ? q_len : p.max_rows;
+  if (row >= wr_len) return;
+  float mw[4], M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    mw[w] = reinterpret_cast<const float*>(lds + w * (kTile * kKRow))[col];
+    M = fmaxf(M, mw[w]);
+  }
+  float L = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* pw = reinterpret_cast<const float*>(lds + w * (kTile * kKRow));
+      const float f = __builtin_amdgcn_exp2f(mw[w] - M);  // 0 for a part with no keys
+      L += f * pw[16 + col];
+      acc += f * *reinterpret_cast<const f32x4*>(pw + 32 + col * kD + d);
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const int64_t base = ((int64_t)(qs + row) * p.Hq + 4 * g + (col & 3)) * kD + d;
+  if (p.out_f32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + base) =
+        make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  } else {
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + base) =
+        u32x2{pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv)};
+  }
+}
+
+// Wave-uniform sum of an int over the 64 lanes (DPP within rows of 16, then
+// the four rows' totals).
+__device__ __forceinline__ int wave_sum_i(int x) {
+  x += __builtin_amdgcn_mov_dpp(x, kQuadXor1, 0xf, 0xf, true);
+  x += __builtin_amdgcn_mov_dpp(x, kQuadXor2, 0xf, 0xf, true);
+  x += __builtin_amdgcn_mov_dpp(x, kRowHalfMirror, 0xf, 0xf, true);
+  x += __builtin_amdgcn_mov_dpp(x, kRowMirror, 0xf, 0xf, true);
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+         __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
+}
+
+// Compact grid (at most kCompactChunks * 64 sequences).  The rank grid gives
+// every sequence tiles_max ranks, and a sequence with fewer query tiles
+// leaves workgroups that only read its lengths and exit; in a mixed batch of
+// decode rows and prompt chunks most of the grid is such workgroups, and
+// while long-lived workgroups hold most of the CU slots they pass through
+// the rest one round trip at a time.  The compact grid enumerates only the
+// live (rank, sequence) pairs, in the rank grid's order (rank, then
+// sequence).  Sequence b with n query tiles is live at
+//   ranks [tiles_max - n, tiles_max)                  without cached history,
+//   rank 0 and ranks [tiles_max - n + 1, tiles_max)   with it (tile 0 first).
+// Workgroup e finds its rank r as the largest r with C(r) <= e, where C(r)
+// counts the live pairs of all ranks below r (a binary search over r; each
+// C is one wave sum), and its sequence as the (e - C(r))-th one live at r.
+// Every wavefront computes the same result (no LDS, no barrier).  Returns
+// false for the few workgroups past the live pairs (the grid is sized from
+// an upper bound of the tile count).
+constexpr int kCompactChunks = 4;
+
+__device__ __forceinline__ bool compact_unit(const PParams& p, int e, int lane, int& b,
+                                             int& rank, int& qs, int& q_len, int& ctx) {
+  const int cap = p.max_blocks * kBS;
+  int s[kCompactChunks], m[kCompactChunks], f[kCompactChunks];
+  int c_qs[kCompactChunks], c_q[kCompactChunks], c_ctx[kCompactChunks];
+#pragma unroll
+  for (int c = 0; c < kCompactChunks; ++c) {
+    const int bb = 64 * c + lane;
+    s[c] = p.tiles_max;  // first rank of the aligned part; m its length
+    m[c] = 0;
+    f[c] = 0;            // 1: tile 0 runs at rank 0 (cached history)
+    c_qs[c] = c_q[c] = c_ctx[c] = 0;
+    if (c < p.chunks && bb < p.B) {  // c < chunks: a uniform branch
+      const int a0 = p.cu_q_lens[bb];
+      const int q = p.cu_q_lens[bb + 1] - a0;
+      int cx = p.context_lens[bb];
+      cx = cx > cap ? cap : cx;
+      const int rows = q < p.max_rows ? q : p.max_rows;
+      const int n = rows > 0 ? (rows + kQRows - 1) / kQRows : 0;
+      c_qs[c] = a0;
+      c_q[c] = q;
+      c_ctx[c] = cx;
+      if (n > 0) {
+        f[c] = cx - q > 0;
+        s[c] = p.tiles_max - n + f[c];
+        m[c] = n - f[c];
+      }
+    }
+  }
+  auto below = [&](int r) {  // live pairs at ranks < r
+    int x = 0;
+#pragma unroll
+    for (int c = 0; c < kCompactChunks; ++c) {
+      if (c < p.chunks) {
+        const int a = r - s[c];
+        x += (f[c] & (r > 0 ? 1 : 0)) + (a < 0 ? 0 : a < m[c] ? a : m[c]);
+      }
+    }
+    return wave_sum_i(x);
+  };
+  if (e >= below(p.tiles_max)) return false;
+  int lo = 0, hi = p.tiles_max;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (below(mid) <= e) lo = mid;
+    else hi = mid;
+  }
+  int j = e - below(lo);
+#pragma unroll
+  for (int c = 0; c < kCompactChunks; ++c) {
+    if (c >= p.chunks) break;
+    const bool live = (lo == 0 && f[c]) || (m[c] > 0 && s[c] <= lo);
+    const uint64_t mask = __builtin_amdgcn_ballot_w64(live);
+    const int pc = __builtin_popcountll(mask);
+    if (j < pc) {
+      const int below_lane = __builtin_amdgcn_mbcnt_hi(
+          (uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+      const uint64_t pick = __builtin_amdgcn_ballot_w64(live && below_lane == j);
+      const int ln = __builtin_ctzll(pick);
+      b = 64 * c + ln;
+      rank = lo;
+      qs = __builtin_amdgcn_readlane(c_qs[c], ln);
+      q_len = __builtin_amdgcn_readlane(c_q[c], ln);
+      ctx = __builtin_amdgcn_readlane(c_ctx[c], ln);
+      return true;
+    }
+    j -= pc;
+  }
+  return false;
+}
+
 __global__ void __launch_bounds__(256, 3)
 prefill_kernel(PParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t ks_buf[2][kTile * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t vs_buf[2][kTile * kKRow];
+  // four 64-key tiles: K and V double buffered (short rows: one V tile per
+  // wavefront)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[4][kTile * kKRow];
+  uint16_t (*ks_buf)[kTile * kKRow] = lds;
+  uint16_t (*vs_buf)[kTile * kKRow] = lds + 2;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -179,20 +518,30 @@ prefill_kernel(PParams p) {
   // history, tile 0 already sees the whole history and can be the heaviest
   // unit of the launch (a decode row of a mixed batch is only tile 0), so
   // it takes the first rank and the other tiles follow from the last down.
+  // The compact grid keeps this order and leaves out the (rank, sequence)
+  // pairs that hold no tile.
   const int g = blockIdx.x % p.Hkv;
   const int rest = blockIdx.x / p.Hkv;
-  const int b = rest % p.B;
-  const int rank = rest / p.B;
-
-  const int qs = p.cu_q_lens[b];
-  const int q_len = p.cu_q_lens[b + 1] - qs;
-  int ctx = p.context_lens[b];
   const int cap = p.max_blocks * kBS;
-  ctx = ctx > cap ? cap : ctx;
+  int b, rank, qs, q_len, ctx;
+  if (p.chunks > 0) {
+    if (!compact_unit(p, rest, lane, b, rank, qs, q_len, ctx)) return;
+  } else {
+    b = rest % p.B;
+    rank = rest / p.B;
+    qs = p.cu_q_lens[b];
+    q_len = p.cu_q_lens[b + 1] - qs;
+    ctx = p.context_lens[b];
+    ctx = ctx > cap ? cap : ctx;
+  }
   const int hist = ctx - q_len;  // position of query row 0 minus 0
   const int tile = hist <= 0 ? p.tiles_max - 1 - rank : rank == 0 ? 0 : p.tiles_max - rank;
   const int q0 = tile * kQRows;
   if (q0 >= q_len) return;
+  if (q_len <= kShortRows) {
+    short_rows(p, &lds[0][0], b, g, qs, q_len, ctx, tid);
+    return;
+  }
   const int rows = q_len - q0 < kQRows ? q_len - q0 : kQRows;
   const int pos_first = hist + q0;
   const int pos_last = hist + q0 + rows - 1;
@@ -354,7 +703,7 @@ prefill_kernel(PParams p) {
   const float lt = l_run + shfl_xor(l_run, 32);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   const int row = q0 + lr;
-  if (row >= q_len) return;
+  if (row >= (q_len < p.max_rows ? q_len : p.max_rows)) return;
   const int64_t base = ((int64_t)(qs + row) * p.Hq + h) * kD;
 #pragma unroll
   for (int dt = 0; dt < 2; ++dt)
@@ -375,10 +724,29 @@ prefill_kernel(PParams p) {
 
 }  // namespace
 
-int64_t prefill_grid_size(int32_t max_q_len, int32_t T_q, int32_t B, int32_t Hkv) {
+namespace {
+// Units of the launch: (rank, sequence) pairs of the rank grid, or, for the
+// compact grid, an upper bound of the query tiles: a sequence of q >= 1 rows
+// has ceil(q / 32) <= 1 + (q - 1) / 32 tiles, so all of them together at most
+// B + T_q / 32.  The compact grid pays its search in every workgroup and
+// starts all live tiles at once; it is used (for at most 256 sequences) where
+// at least 7 of every 8 units of the rank grid would be dead, i.e. where the
+// bound is at most 1/8 of the rank grid.  chunks is 0 for the rank grid.
+constexpr int64_t kCompactRatio = 8;
+
+int64_t prefill_units(int32_t max_q_len, int32_t T_q, int32_t B, int* chunks) {
   // no prompt is longer than all the query tokens together
   const int64_t rows = max_q_len < T_q ? max_q_len : T_q;
-  return (rows + kQRows - 1) / kQRows * B * Hkv;
+  const int64_t ranked = (rows + kQRows - 1) / kQRows * B;
+  const int64_t bound = (int64_t)B + T_q / kQRows;
+  const bool compact = B <= 64 * kCompactChunks && bound * kCompactRatio <= ranked;
+  if (chunks) *chunks = compact ? (B + 63) / 64 : 0;
+  return compact ? bound : ranked;
+}
+}  // namespace
+
+int64_t prefill_grid_size(int32_t max_q_len, int32_t T_q, int32_t B, int32_t Hkv) {
+  return prefill_units(max_q_len, T_q, B, nullptr) * Hkv;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
@@ -398,12 +766,13 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
   p.num_blocks = a.num_blocks;
   const int32_t rows = a.max_q_len < a.T_q ? a.max_q_len : a.T_q;
   p.tiles_max = (rows + kQRows - 1) / kQRows;
+  p.max_rows = rows;
   // |scale| in log2 units, floored so that a zero scale still maps masked
   // (-inf) scores to -inf instead of NaN; any real score times 1e-30 is 0.
   p.c_log2 = (a.scale < 0.f ? -a.scale : a.scale) * kLog2e;
   if (p.c_log2 < 1e-30f) p.c_log2 = 1e-30f;
   p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
-  const int64_t grid = prefill_grid_size(a.max_q_len, a.T_q, a.B, a.Hkv);
+  const int64_t grid = prefill_units(a.max_q_len, a.T_q, a.B, &p.chunks) * a.Hkv;
   hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

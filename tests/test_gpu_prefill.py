@@ -187,3 +187,125 @@ def test_rows_past_max_q_len_untouched(history):
         done[cu[b]:min(cu[b + 1], cu[b] + 64)] = True
     assert_close(got[done], ref[done], f"prefill max_q_len 64 hist {history}")
     assert np.isnan(got[~done]).all()
+
+
+# Sequences with at most 4 query rows take the short-row path: the four
+# wavefronts of the workgroup split the context's blocks and the partial
+# results are combined by log-sum-exp.  Contexts below, at and past block and
+# 64-key boundaries, shorter than one block per wavefront, and long.
+@pytest.mark.parametrize("prompts,history", [
+    ([1, 2, 3, 4, 5], [2000, 777, 64, 15, 300]),
+    ([1] * 12 + [256], [0, 1, 15, 16, 17, 63, 64, 65, 129, 1023, 4095, 300, 700]),
+    ([4, 3, 1, 2], [0, 0, 0, 1]),
+])
+def test_short_rows(prompts, history):
+    p = wl.prefill_case(prompts=prompts, history=history, num_blocks=1024, seed=77, poison=True)
+    k, v, kr, vr = appended(p)
+    ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
+                                p.cu_q_lens.numpy(), p.scale, threads=_threads())
+    got = gpu_prefill(p, k, v)
+    assert_close(got.cpu().numpy(), ref, f"short rows {prompts} hist {history}")
+    got16 = gpu_prefill(p, k, v, torch.bfloat16)
+    assert_close_bf16(got16.cpu(), ref, f"short rows {prompts}")
+
+
+def test_short_rows_context_shorter_than_rows():
+    """Short rows whose position is negative see no key: zero rows, beside
+    rows of the same sequence that see a few."""
+    p = wl.prefill_case(prompts=[4, 3, 2, 1], num_blocks=64, seed=76)
+    p.context_lens = torch.tensor([2, 0, 1, 0], dtype=torch.int32)
+    k, v = dev(p.k_cache), dev(p.v_cache)
+    ref = oracle.prefill_causal(u16(p.q), u16(p.k_cache), u16(p.v_cache), p.block_tables.numpy(),
+                                p.context_lens.numpy(), p.cu_q_lens.numpy(), p.scale)
+    got = gpu_prefill(p, k, v).cpu()
+    zero = [0, 1, 4, 5, 6, 7, 9]  # positions -2, -1 | -3, -2, -1 | -1 | -1
+    assert torch.all(got[zero] == 0)
+    assert_close(got.numpy(), ref, "short rows, short context")
+
+
+@pytest.mark.parametrize("slope", [0.15, -0.15])
+def test_short_rows_monotone_history(slope):
+    """Cached keys whose scores rise (or fall) along the context: the short-row
+    path's per-group maximum moves on every group of every wavefront (or the
+    first key dominates and later weights underflow)."""
+    p = wl.prefill_case(prompts=[1, 2, 4], history=[900, 333, 64], num_blocks=256, seed=78,
+                        poison=True)
+    D, bs = p.q.shape[-1], p.block_size
+    p.q.fill_(0.25)
+    p.k_new.fill_(0.0)
+    for b, L in enumerate(p.context_lens.tolist()):
+        j = torch.arange(L, dtype=torch.float32)
+        kval = (slope * j / (p.scale * D * 0.25)).to(torch.bfloat16)
+        for key in range(L):
+            p.k_cache[int(p.block_tables[b, key // bs]), :, key % bs, :] = kval[key]
+    k, v, kr, vr = appended(p)
+    ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
+                                p.cu_q_lens.numpy(), p.scale)
+    got = gpu_prefill(p, k, v)
+    assert_close(got.cpu().numpy(), ref, f"short rows monotone slope {slope}")
+
+
+def test_rows_past_max_q_len_not_a_tile_multiple():
+    """max_q_len of 2 (short rows and a 50-row prompt) and of 50: rows at and
+    past max_q_len are not written, also inside a query tile."""
+    p = wl.prefill_case(prompts=[3, 4, 1, 50, 70], history=[100, 0, 30, 10, 5], num_blocks=64,
+                        seed=79, poison=True)
+    k, v, kr, vr = appended(p)
+    ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
+                                p.cu_q_lens.numpy(), p.scale)
+    cu = p.cu_q_lens.tolist()
+    for mq in (2, 50):
+        out = torch.full(tuple(p.q.shape), float("nan"), dtype=torch.float32, device="cuda")
+        pkv.paged_attention_prefill_causal(out, dev(p.q), k, v, dev(p.block_tables),
+                                           dev(p.context_lens), dev(p.cu_q_lens), p.scale, mq)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        done = np.zeros(got.shape[0], dtype=bool)
+        for b in range(len(cu) - 1):
+            done[cu[b]:min(cu[b + 1], cu[b] + mq)] = True
+        assert_close(got[done], ref[done], f"prefill max_q_len {mq}")
+        assert np.isnan(got[~done]).all()
+
+
+def test_mixed_batch_every_row():
+    """The mixed continuous batch of the benchmark (60 decoding sequences with
+    contexts log-uniform in [16, 2048] and 4 chunks of 256 tokens on 768
+    cached ones) in one launch: every row and head against the oracle."""
+    g = wl.generator(21)
+    dec_lens = wl.draw_lens(g, 60, ("loguniform", 16, 2048)).tolist()
+    prompts = [1] * 60 + [256] * 4
+    history = [int(L) - 1 for L in dec_lens] + [768] * 4
+    p = wl.prefill_case(seed=21, prompts=prompts, history=history, num_blocks=8192)
+    k, v, kr, vr = appended(p)
+    ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
+                                p.cu_q_lens.numpy(), p.scale, threads=_threads())
+    got16 = gpu_prefill(p, k, v, torch.bfloat16)
+    assert_close_bf16(got16.cpu(), ref, "mixed batch, every row")
+
+
+@pytest.mark.parametrize("B,long_len,compact", [
+    (65, 512, True), (200, 512, True), (256, 640, True),   # 2, 4 and 4 chunks of 64
+    (300, 512, False),                                     # more than 256 sequences
+    (64, 100, False),                                      # few dead units
+])
+def test_many_sequences_either_grid(B, long_len, compact):
+    """Short rows, 33-row prompts and empty ones beside two long prompts (one
+    with cached history): where nearly every unit of the grid of all ranks of
+    all sequences would be dead (at most 256 sequences), only the live query
+    tiles are launched; otherwise every rank of every sequence.  All rows
+    against the oracle."""
+    rng = np.random.default_rng(80 + B)
+    prompts = rng.choice([0, 1, 1, 1, 2, 3, 4, 5, 33], size=B).tolist()
+    history = [int(x) for x in rng.integers(0, 400, size=B)]
+    prompts[3] = prompts[B - 2] = long_len
+    history[B - 2] = 0
+    T = sum(prompts)
+    ranked = (min(long_len, T) + 31) // 32 * B
+    assert (B <= 256 and 8 * (B + T // 32) <= ranked) == compact
+    p = wl.prefill_case(prompts=prompts, history=history, num_blocks=B * 34, seed=80 + B,
+                        poison=True)
+    k, v, kr, vr = appended(p)
+    ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
+                                p.cu_q_lens.numpy(), p.scale, threads=_threads())
+    got = gpu_prefill(p, k, v)
+    assert_close(got.cpu().numpy(), ref, f"{B} sequences")
