@@ -421,8 +421,10 @@ __device__ __forceinline__ int wave_sum_i(int x) {
 // the rest one round trip at a time.  The compact grid enumerates only the
 // live (rank, sequence) pairs, in the rank grid's order (rank, then
 // sequence).  Sequence b with n query tiles is live at
-//   ranks [tiles_max - n, tiles_max)                  without cached history,
-//   rank 0 and ranks [tiles_max - n + 1, tiles_max)   with it (tile 0 first).
+//   ranks [tiles_max - n, tiles_max)                  without cached history
+//                                                     or with at most
+//                                                     kShortRows rows,
+//   rank 0 and ranks [tiles_max - n + 1, tiles_max)   otherwise (tile 0 first).
 // Workgroup e finds its rank r as the largest r with C(r) <= e, where C(r)
 // counts the live pairs of all ranks below r (a binary search over r; each
 // C is one wave sum), and its sequence as the (e - C(r))-th one live at r.
@@ -454,7 +456,7 @@ __device__ __forceinline__ bool compact_unit(const PParams& p, int e, int lane, 
       c_q[c] = q;
       c_ctx[c] = cx;
       if (n > 0) {
-        f[c] = cx - q > 0;
+        f[c] = cx - q > 0 && q > kShortRows;
         s[c] = p.tiles_max - n + f[c];
         m[c] = n - f[c];
       }
@@ -518,8 +520,11 @@ prefill_kernel(PParams p) {
   // history, tile 0 already sees the whole history and can be the heaviest
   // unit of the launch (a decode row of a mixed batch is only tile 0), so
   // it takes the first rank and the other tiles follow from the last down.
-  // The compact grid keeps this order and leaves out the (rank, sequence)
-  // pairs that hold no tile.
+  // A sequence of at most kShortRows rows (one short-row workgroup) takes
+  // the last rank: its workgroup streams the context and is long-lived, so
+  // it starts after the prompts' tiles, and its dead ranks pass through
+  // while the CUs still have free slots.  The compact grid keeps this order
+  // and leaves out the (rank, sequence) pairs that hold no tile.
   const int g = blockIdx.x % p.Hkv;
   const int rest = blockIdx.x / p.Hkv;
   const int cap = p.max_blocks * kBS;
@@ -535,7 +540,8 @@ prefill_kernel(PParams p) {
     ctx = ctx > cap ? cap : ctx;
   }
   const int hist = ctx - q_len;  // position of query row 0 minus 0
-  const int tile = hist <= 0 ? p.tiles_max - 1 - rank : rank == 0 ? 0 : p.tiles_max - rank;
+  const int tile = hist <= 0 || q_len <= kShortRows ? p.tiles_max - 1 - rank
+                   : rank == 0 ? 0 : p.tiles_max - rank;
   const int q0 = tile * kQRows;
   if (q0 >= q_len) return;
   if (q_len <= kShortRows) {
