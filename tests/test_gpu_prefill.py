@@ -309,3 +309,49 @@ def test_many_sequences_either_grid(B, long_len, compact):
                                 p.cu_q_lens.numpy(), p.scale, threads=_threads())
     got = gpu_prefill(p, k, v)
     assert_close(got.cpu().numpy(), ref, f"{B} sequences")
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_batches(seed):
+    """Seeded random batch compositions: short rows (1-4), prompts across
+    query-tile edges, empty sequences, cached history from none to past a
+    64-key group, and max_q_len at or below the longest prompt, so that both
+    grids (odd seeds: mostly short rows beside one or two long prompts, where
+    most of the rank grid would be dead), the short-row path and the
+    written-row limit meet.  Every written row against the oracle; rows past
+    max_q_len keep the NaN they held."""
+    rng = np.random.default_rng(1000 + seed)
+    if seed % 2:
+        B = int(rng.integers(24, 64))
+        kinds = rng.choice(["short"] * 12 + ["tile", "empty"], size=B)
+        kinds[:int(rng.integers(1, 3))] = "huge"
+    else:
+        B = int(rng.integers(1, 48))
+        kinds = rng.choice(["short", "short", "tile", "long", "empty"], size=B)
+    prompts = [int(rng.integers(1, 5)) if k == "short" else
+               int(rng.integers(5, 70)) if k == "tile" else
+               int(rng.integers(70, 300)) if k == "long" else
+               int(rng.integers(300, 700)) if k == "huge" else 0 for k in kinds]
+    if sum(prompts) == 0:
+        prompts[0] = 1
+    history = [int(rng.choice([0, 0, int(rng.integers(1, 70)), int(rng.integers(70, 700))]))
+               for _ in range(B)]
+    mq_full = max(prompts)
+    mq = mq_full if rng.random() < 0.6 else int(rng.integers(1, mq_full + 1))
+    p = wl.prefill_case(prompts=prompts, history=history, num_blocks=B * 80 + 128,
+                        seed=2000 + seed, poison=True)
+    k, v, kr, vr = appended(p)
+    ref = oracle.prefill_causal(u16(p.q), kr, vr, p.block_tables.numpy(), p.context_lens.numpy(),
+                                p.cu_q_lens.numpy(), p.scale, threads=_threads())
+    out = torch.full(tuple(p.q.shape), float("nan"), dtype=torch.float32, device="cuda")
+    print(f"  seed {seed}: B {B}, max_q_len {mq} of {mq_full}, T {sum(prompts)}", flush=True)
+    pkv.paged_attention_prefill_causal(out, dev(p.q), k, v, dev(p.block_tables),
+                                       dev(p.context_lens), dev(p.cu_q_lens), p.scale, mq)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    cu = p.cu_q_lens.tolist()
+    done = np.zeros(got.shape[0], dtype=bool)
+    for b in range(B):
+        done[cu[b]:min(cu[b + 1], cu[b] + mq)] = True
+    assert_close(got[done], ref[done], f"random batch {seed}")
+    assert np.isnan(got[~done]).all()
