@@ -92,6 +92,54 @@ def source_hash(*names):
     return h.hexdigest()[:16]
 
 
+def parse_dpm(text):
+    """A DPM clock table as the amdgpu driver prints it ("S: 125Mhz *",
+    "1: 2400Mhz", one level a line, '*' on the current one): (levels in MHz,
+    current level or None)."""
+    levels, cur = [], None
+    for line in text.splitlines():
+        parts = line.split()
+        if len(parts) < 2 or not parts[1].lower().endswith("mhz"):
+            continue
+        mhz = int(parts[1][:-3])
+        levels.append(mhz)
+        if parts[-1] == "*":
+            cur = mhz
+    return levels, cur
+
+
+def gpu_clocks(torch, busy, samples=8):
+    """The GPU the legs ran on, and its shader (sclk) and memory (mclk)
+    clocks as the driver reports them: the DPM levels from the device's sysfs
+    tables, and the level marked current, sampled every 5 ms while `busy()`
+    has untimed work queued.  Clock fields are null where the tables cannot
+    be read."""
+    p = torch.cuda.get_device_properties(0)
+    rec = {"name": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+           "source": "sysfs pp_dpm_sclk / pp_dpm_mclk of the device, sampled during "
+                     "untimed step replays after the timed region"}
+    path = (f"/sys/bus/pci/devices/{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:"
+            f"{p.pci_device_id:02x}.0")
+
+    def read(name):
+        with open(os.path.join(path, name)) as f:
+            return parse_dpm(f.read())
+
+    busy()
+    try:
+        seen = {"sclk": [], "mclk": []}
+        for _ in range(samples):
+            time.sleep(0.005)
+            for k in seen:
+                seen[k].append(read(f"pp_dpm_{k}")[1])
+        for k in seen:
+            rec[f"{k}_mhz"] = {"levels": read(f"pp_dpm_{k}")[0], "current_under_load": seen[k]}
+    except (OSError, ValueError):
+        rec["sclk_mhz"] = rec["mclk_mhz"] = None
+    torch.cuda.synchronize()
+    return rec
+
+
 def decode_bytes(lens, B, Hq, Hkv, D, out_bytes, bs=16):
     """Algorithmic HBM bytes of one decode call: K+V of every context token
     (2 * Hkv * D * 2 = 2048 B per token at 8 KV heads), q, out, block ids, lens."""
@@ -695,6 +743,7 @@ def main():
         return ev0.elapsed_time(ev1) * 1e3 / (args.steps * calls)
 
     decode_us = event_us(graphs["decode"], LAYERS)
+    device = gpu_clocks(torch, lambda: [graphs["step"].replay() for _ in range(100)])
     other_ms = {f: round(event_us(graphs[f], 1) * 1e-3, 4) for f in others}
     lens_list = case.context_lens.tolist()
     dec_b = decode_bytes(lens_list, B, Hq, Hkv, D, 2)
@@ -749,6 +798,7 @@ def main():
                      "kernel_source_hash": khash},
         "other_step_forms_ms_per_step": other_ms,
         "decode_only_us_per_call": round(decode_us, 2),
+        "device": device,
     }
     # the same K/V bytes through the same tables, read by a plain streaming kernel
     fl_us, fl_b = run_floor(torch, pkv, case, k_layers, v_layers, args.steps, 3)

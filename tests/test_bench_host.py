@@ -67,3 +67,12 @@ def test_committed_traffic_matches_the_committed_decode_source():
     the benchmark reports it (a stale file would make traffic null)."""
     h = bench.source_hash("decode.hip")
     assert bench.traffic_from_profiles(h, "planned") is not None
+
+
+def test_dpm_clock_tables_parse():
+    """The driver's DPM tables as printed on the GPU host: levels in MHz and
+    the one marked current ('S' is the sleep level)."""
+    assert bench.parse_dpm("S: 125Mhz *\n0: 500Mhz\n1: 2400Mhz\n") == ([125, 500, 2400], 125)
+    assert bench.parse_dpm("0: 500Mhz\n1: 2400Mhz *\n") == ([500, 2400], 2400)
+    assert bench.parse_dpm("0: 2000Mhz *\n") == ([2000], 2000)
+    assert bench.parse_dpm("") == ([], None)
