@@ -303,6 +303,34 @@ def run_prefill(torch, pkv, wl, steps, warmup, copies=8):
                          "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}}
 
 
+def run_mfma_probe(torch, pkv, iters=20000, launches=10):
+    """pagedkv_mfma_probe: bf16 MFMA chains and nothing else on 2048
+    wavefronts, `launches` launches of `iters` rounds timed with HIP events
+    after a warm-up; the issue rate the prefill's flops are measured against,
+    taken at the GPU's running clock (sampled during untimed launches)."""
+    sink = torch.empty(pkv.STREAM_SINK_BYTES // 4, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        pkv.mfma_probe(iters, sink)
+    torch.cuda.synchronize()
+    if not torch.all(sink == 4.0 * iters):
+        raise RuntimeError("mfma probe: the folded result is not 4 * iters")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(launches):
+        pkv.mfma_probe(iters, sink)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) * 1e3 / launches
+    tflops = pkv.mfma_probe_flops(iters) / (us * 1e-6) / 1e12
+    clocks = gpu_clocks(torch, lambda: [pkv.mfma_probe(iters, sink) for _ in range(20)])
+    return {"kernel": "mfma_probe_kernel (pagedkv_mfma_probe): 2048 wavefronts x 4 chains of "
+                      f"v_mfma_f32_32x32x16_bf16, {iters} rounds, operands in registers",
+            "us_per_call": round(us, 2), "flops": pkv.mfma_probe_flops(iters),
+            "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "sclk_mhz_under_load": (clocks.get("sclk_mhz") or {}).get("current_under_load")}
+
+
 def run_floor(torch, pkv, case, k_layers, v_layers, steps, warmup):
     """pagedkv_stream_blocks over the blocks the batch's contexts use (every
     KV head of each), one call per pool pair in turn: a plain streaming read
@@ -814,6 +842,10 @@ def main():
     if not args.no_prefill:
         try:
             result["prefill"] = run_prefill(torch, pkv, wl, max(args.steps, 10), args.warmup)
+            probe = run_mfma_probe(torch, pkv)
+            probe["prefill_over_probe"] = round(
+                result["prefill"]["roofline"]["achieved"] / probe["achieved"], 4)
+            result["prefill"]["mfma_probe"] = probe
         except pkv.PagedKVError as e:
             result["prefill"] = {"error": str(e)}
 

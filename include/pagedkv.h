@@ -515,6 +515,27 @@ PKV_API int pagedkv_stream_blocks(const void *k_cache, const void *v_cache,
                           int32_t D, int32_t block_size, int32_t num_blocks, void *sink,
                           size_t sink_bytes, void *stream);
 
+/* pagedkv_mfma_probe -- run bf16 matrix-core products and nothing else: the
+ * issue rate that the prefill kernel's flops are measured against, taken on
+ * this GPU at its running clock.
+ *
+ * Defined by: guide ch. 6 "Prefill vs Decode" (prefill is compute bound) and
+ * ch. 11 "Benchmarks" (state how close a kernel comes to its bound).  Not
+ * part of the attention path.
+ *
+ * 2048 wavefronts each run 4 independent chains of
+ * v_mfma_f32_32x32x16_bf16 (32,768 flops a product) `iters` times on
+ * operands held in registers: 2048 * 4 * iters * 32768 flops per launch.
+ * iters         1 .. PKV_MFMA_PROBE_MAX_ITERS.
+ * sink          device buffer of at least PKV_STREAM_SINK_BYTES, 16-byte
+ *               aligned; lane l of wavefront w writes float w * 64 + l, whose
+ *               value is exactly 4 * iters (every operand element is 2^-4).
+ * Errors: PKV_ERR_INVALID_ARG for iters out of range or a null or misaligned
+ * sink, PKV_ERR_WORKSPACE for a short sink.
+ */
+#define PKV_MFMA_PROBE_MAX_ITERS (1 << 18)
+PKV_API int pagedkv_mfma_probe(int32_t iters, void *sink, size_t sink_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,7 +49,7 @@ ABI_SYMBOLS = ("pagedkv_last_error", "pagedkv_check_tables", "kv_append", "kv_ap
                "paged_attention_decode", "paged_attention_decode_append",
                "paged_attention_decode_noalloc",
                "paged_attention_decode_plan",
-               "paged_attention_prefill_causal", "pagedkv_stream_blocks",
+               "paged_attention_prefill_causal", "pagedkv_stream_blocks", "pagedkv_mfma_probe",
                "pkv_sched_create", "pkv_sched_destroy", "pkv_sched_add_request",
                "pkv_sched_step", "pkv_sched_events", "pkv_sched_stats",
                "pkv_sched_add_request_prefix", "pkv_sched_fork", "pkv_sched_copies")
@@ -154,6 +154,8 @@ def load_library():
     lib.paged_attention_prefill_causal.restype = ctypes.c_int
     lib.pagedkv_stream_blocks.argtypes = [P, P, P, I, I, I, I, I, P, Z, P]
     lib.pagedkv_stream_blocks.restype = ctypes.c_int
+    lib.pagedkv_mfma_probe.argtypes = [I, P, Z, P]
+    lib.pagedkv_mfma_probe.restype = ctypes.c_int
     _bind_host(lib)
     _lib = lib
     return lib
@@ -455,6 +457,24 @@ def stream_blocks(k_cache, v_cache, block_ids, sink):
         _dev(k_cache, torch.bfloat16, "k_cache"), _dev(v_cache, torch.bfloat16, "v_cache"),
         _dev(block_ids, torch.int32, "block_ids"), block_ids.numel(), Hkv, D, bs, N,
         _dev(sink, torch.uint8, "sink"), sink.numel(), _stream()))
+
+
+MFMA_PROBE_MAX_ITERS = 1 << 18
+
+
+def mfma_probe(iters, sink):
+    """Measurement probe: 2048 wavefronts of bf16 MFMA chains, `iters` rounds
+    each; sink is a float32 device tensor of at least STREAM_SINK_BYTES / 4
+    elements and receives exactly 4 * iters in each."""
+    torch = _torch()
+    _check(load_library().pagedkv_mfma_probe(
+        int(iters), _dev(sink, torch.float32, "sink"), sink.numel() * 4, _stream()))
+
+
+def mfma_probe_flops(iters):
+    """Flops of one mfma_probe launch: 2048 wavefronts x 4 chains x iters
+    products of 32 x 32 x 16."""
+    return 2048 * 4 * int(iters) * 2 * 32 * 32 * 16
 
 
 class Scheduler:

@@ -591,4 +591,17 @@ int pagedkv_stream_blocks(const void* k_cache, const void* v_cache, const int32_
                     "pagedkv_stream_blocks launch");
 }
 
+int pagedkv_mfma_probe(int32_t iters, void* sink, size_t sink_bytes, void* stream) {
+  if (iters <= 0 || iters > PKV_MFMA_PROBE_MAX_ITERS)
+    return fail(PKV_ERR_INVALID_ARG, "iters must be in [1, %d] (got %d)", PKV_MFMA_PROBE_MAX_ITERS,
+                iters);
+  if (!sink) return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(sink)) return fail(PKV_ERR_INVALID_ARG, "sink must be 16-byte aligned");
+  const size_t need = (size_t)pkv::stream_blocks_sink_words() * 4;
+  if (sink_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, "sink of %zu bytes needed, %zu given", need, sink_bytes);
+  return hip_status(pkv::launch_mfma_probe(iters, static_cast<float*>(sink), (hipStream_t)stream),
+                    "pagedkv_mfma_probe launch");
+}
+
 }  // extern "C"

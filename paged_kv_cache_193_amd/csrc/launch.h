@@ -152,6 +152,11 @@ int64_t prefill_grid_size(int32_t max_q_len, int32_t T_q, int32_t B, int32_t Hkv
 // list of block ids (probe.hip); `sink` receives stream_blocks_sink_words()
 // words.
 int64_t stream_blocks_sink_words();
+// MFMA issue-rate probe (probe.hip): kProbeWaves wavefronts of bf16 MFMA
+// chains, `iters` rounds each; flops of one launch, and the launch itself.
+// `sink` receives stream_blocks_sink_words() floats.
+int64_t mfma_probe_flops(int32_t iters);
+hipError_t launch_mfma_probe(int32_t iters, float* sink, hipStream_t stream);
 hipError_t launch_stream_blocks(const void* k_cache, const void* v_cache, const int32_t* block_ids,
                                 int32_t n_ids, int32_t Hkv, int32_t D, int32_t block_size,
                                 int32_t num_blocks, uint32_t* sink, hipStream_t stream);

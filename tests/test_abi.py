@@ -447,3 +447,17 @@ def test_noalloc_scratch_fits_the_automatic_split(lib):
     assert 0 < need <= 16 << 20
     assert noalloc_call(lib, B=0, out=None, q=None, k=None, v=None, bt=None, cl=None,
                         part=-1) == pkv.PKV_OK
+
+
+@pytest.mark.parametrize("iters,sink,nbytes,code", [
+    (0, 16, pkv.STREAM_SINK_BYTES, -1),
+    (pkv.MFMA_PROBE_MAX_ITERS + 1, 16, pkv.STREAM_SINK_BYTES, -1),
+    (8, None, pkv.STREAM_SINK_BYTES, -1),
+    (8, 20, pkv.STREAM_SINK_BYTES, -1),
+    (8, 16, pkv.STREAM_SINK_BYTES - 4, -3),
+])
+def test_mfma_probe_rejects(lib, iters, sink, nbytes, code):
+    """The MFMA probe checks its iteration count and sink on the host (bad
+    arguments never reach the device; the fake sink addresses are not read)."""
+    assert lib.pagedkv_mfma_probe(iters, sink, nbytes, None) == code
+    assert lib.pagedkv_last_error()
