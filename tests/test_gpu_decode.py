@@ -269,3 +269,78 @@ def test_largest_batch_of_the_automatic_split():
         torch.cuda.synchronize()
         assert_close(out.cpu().numpy(), ref, f"B=4096 mode={mode}")
         assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0   # counters left at zero
+
+
+def _random_lens(rng, B):
+    kinds = rng.choice(["zero", "edge", "short", "mid", "long"], size=B,
+                       p=[0.05, 0.2, 0.3, 0.3, 0.15])
+    out = []
+    for k in kinds:
+        if k == "zero":
+            out.append(0)
+        elif k == "edge":
+            out.append(int(rng.choice([1, 15, 16, 17, 63, 64, 65, 511, 512, 513])))
+        elif k == "short":
+            out.append(int(rng.integers(1, 64)))
+        elif k == "mid":
+            out.append(int(rng.integers(64, 700)))
+        else:
+            out.append(int(rng.integers(700, 3000)))
+    return out
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_batches(seed):
+    """Seeded random batches (1 to 260 sequences, so past the 192 beyond
+    which the automatic split's grid grows; empty, edge, short and long
+    contexts mixed; unused slots NaN): the automatic split, the planned form
+    with its plan, a fixed partition and the append form that stores each
+    sequence's last token again, all against one oracle run on every row, with
+    the split counters back at zero and the pools unchanged."""
+    rng = np.random.default_rng(3000 + seed)
+    B = int(rng.integers(1, 261)) if seed % 3 else int(rng.integers(193, 261))
+    lens = _random_lens(rng, B)
+    need = int(wl.blocks_needed(torch.tensor(lens, dtype=torch.int32), 16).sum())
+    N, maxb = need + 8, max(1, max((n + 15) // 16 for n in lens))
+    c = wl.decode_case("llama1b", seed=4000 + seed, B=B, lens=("fixed", 0), num_blocks=N,
+                       max_blocks=maxb)
+    lens_t = torch.tensor(lens, dtype=torch.int32)
+    c.context_lens = lens_t
+    c.block_tables = wl.tables_from_permutation(wl.generator(5000 + seed), lens_t, 16, N, maxb,
+                                                filler=N - 1)
+    wl.poison_unused(c)
+    ref = oracle.decode(u16(c.q), u16(c.k_cache), u16(c.v_cache), c.block_tables.numpy(),
+                        lens_t.numpy(), c.scale, threads=8)
+    mx = max(1, max(lens)) + int(rng.integers(0, 64))
+    part = int(rng.choice([16, 32, 128, 512]))
+    print(f"  seed {seed}: B {B}, tokens {sum(lens)}, max_context_len {mx}, partition {part}",
+          flush=True)
+    k, v, q, t, l = dev(c.k_cache), dev(c.v_cache), dev(c.q), dev(c.block_tables), dev(lens_t)
+    for mode in (pkv.PARTITION_AUTO, pkv.PARTITION_PLANNED, part):
+        ws = pkv.decode_workspace(B, c.Hq, c.D, mx, mode, "cuda")
+        if mode == pkv.PARTITION_PLANNED:
+            pkv.paged_attention_decode_plan(k, t, l, c.Hq, mx, ws)
+        out = torch.full((B, c.Hq, c.D), float("nan"), dtype=torch.float32, device="cuda")
+        pkv.paged_attention_decode(out, q, k, v, t, l, c.scale, mx, mode, ws)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), ref, f"random seed {seed} mode {mode}")
+        if mode < 0:
+            assert int(ws[:COUNTER_BYTES].view(torch.int32).abs().sum()) == 0
+    # append form: store each non-empty sequence's last token again (pools
+    # unchanged), automatic split; empty sequences store nothing
+    nz = [b for b in range(B) if lens[b] > 0]
+    kn = torch.zeros((B, c.Hkv, c.D), dtype=torch.bfloat16)
+    vn = torch.zeros_like(kn)
+    for b in nz:
+        blk = int(c.block_tables[b, (lens[b] - 1) // 16])
+        kn[b] = c.k_cache[blk, :, (lens[b] - 1) % 16]
+        vn[b] = c.v_cache[blk, :, (lens[b] - 1) % 16]
+    ws = pkv.decode_workspace(B, c.Hq, c.D, mx, pkv.PARTITION_AUTO, "cuda")
+    out = torch.full((B, c.Hq, c.D), float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_attention_decode_append(out, q, k, v, dev(kn), dev(vn), t, l, c.scale, mx,
+                                      pkv.PARTITION_AUTO, ws)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, f"random seed {seed} append")
+    kk, vv = k.cpu(), v.cpu()
+    assert torch.equal(kk.view(torch.int16), c.k_cache.view(torch.int16))
+    assert torch.equal(vv.view(torch.int16), c.v_cache.view(torch.int16))
