@@ -473,7 +473,7 @@ PKV_API int paged_attention_decode_append(void *out, int32_t out_dtype, const vo
  * rows (a decoding sequence of a mixed batch, a few draft tokens) is one
  * workgroup per KV head whose 4 wavefronts split its context.  The grid has
  * ceil(min(max_q_len, T_q) / 32) ranks per sequence, or, for at most 256
- * sequences where at most 1/8 of those would hold a query tile, only
+ * sequences where at most a third of those would hold a query tile, only
  * B + T_q / 32 units per KV head (the tiles of a rank found on the device);
  * a grid beyond one launch (2^32 - 1 work-items) returns
  * PKV_ERR_UNSUPPORTED.

@@ -734,11 +734,11 @@ namespace {
 // Units of the launch: (rank, sequence) pairs of the rank grid, or, for the
 // compact grid, an upper bound of the query tiles: a sequence of q >= 1 rows
 // has ceil(q / 32) <= 1 + (q - 1) / 32 tiles, so all of them together at most
-// B + T_q / 32.  The compact grid pays its search in every workgroup and
-// starts all live tiles at once; it is used (for at most 256 sequences) where
-// at least 7 of every 8 units of the rank grid would be dead, i.e. where the
-// bound is at most 1/8 of the rank grid.  chunks is 0 for the rank grid.
-constexpr int64_t kCompactRatio = 8;
+// B + T_q / 32.  The compact grid pays its search in every workgroup; it is
+// used (for at most 256 sequences) where at least two of every three units
+// of the rank grid would be dead, i.e. where the bound is at most a third of
+// the rank grid.  chunks is 0 for the rank grid.
+constexpr int64_t kCompactRatio = 3;
 
 int64_t prefill_units(int32_t max_q_len, int32_t T_q, int32_t B, int* chunks) {
   // no prompt is longer than all the query tokens together
