@@ -62,7 +62,7 @@ extern "C" {
 
 #define PKV_OK 0
 #define PKV_ERR_INVALID_ARG (-1) /* null pointer, negative or inconsistent size */
-#define PKV_ERR_UNSUPPORTED (-2) /* shape this build does not implement         */
+#define PKV_ERR_UNSUPPORTED (-2) /* shape this library does not implement        */
 #define PKV_ERR_WORKSPACE (-3)   /* workspace missing or too small              */
 #define PKV_ERR_HIP (-4)         /* a HIP runtime call or kernel launch failed  */
 
@@ -158,7 +158,7 @@ PKV_API int kv_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_bloc
  *
  * Defined by: README feature list and table of contents "RoPE" (the model's
  * positional encoding), with kv_append's slot rule above.  The pages name
- * RoPE without a formula; this build takes the rotary embedding of the
+ * RoPE without a formula; this library takes the rotary embedding of the
  * model they run, in the layout of its Safetensors checkpoint: for i < D/2
  * the pair (x[i], x[i + D/2]) of a q or k row is turned by the angle of the
  * token's absolute position pos (kv_append's rule),
@@ -179,7 +179,7 @@ PKV_API int kv_copy_blocks(void *k_cache, void *v_cache, const int32_t *src_bloc
  * A token whose position lies outside [0, max_position) is left alone (no
  * rotation of its q rows, no store of its K/V rows).  Rows whose slot falls
  * outside the table or pool are not stored (their q rows are still rotated).
- * This build implements D == 64 (PKV_ERR_UNSUPPORTED otherwise); pools, rows
+ * This library implements D == 64 (PKV_ERR_UNSUPPORTED otherwise); pools, rows
  * and tables must be 16-byte aligned.
  */
 PKV_API int kv_append_rope(void *k_cache, void *v_cache, void *q, const void *k_new,
@@ -301,7 +301,7 @@ PKV_API int pkv_sched_stats(const pkv_scheduler *s, int64_t *out);
  * so the size of the scratch the split needs is a query.
  *
  * B, Hq, D, max_context_len, partition_size as for paged_attention_decode.
- * This build implements one GQA group (Hq == 4 * Hkv) and one block size
+ * This library implements one GQA group (Hq == 4 * Hkv) and one block size
  * (16), so the KV head count is Hq / 4 and the block size 16.  Pure function
  * of its arguments; makes no HIP call.  Returns 0 (and sets
  * pagedkv_last_error) for arguments decode would reject.
@@ -354,7 +354,7 @@ PKV_API size_t paged_attention_decode_workspace_size(int32_t B, int32_t Hq, int3
  *               for a fixed partition_size, one per wavefront of the grid
  *               for PKV_PARTITION_AUTO);
  *               beyond either limit the call returns PKV_ERR_UNSUPPORTED.
- * This build implements D == 64, block_size == 16 and Hq == 4 * Hkv
+ * This library implements D == 64, block_size == 16 and Hq == 4 * Hkv
  * (PKV_ERR_UNSUPPORTED otherwise).  Empty contexts give zero rows.
  */
 PKV_API int paged_attention_decode(void *out, int32_t out_dtype, const void *q,
@@ -467,7 +467,7 @@ PKV_API int paged_attention_decode_append(void *out, int32_t out_dtype, const vo
  *               (values above T_q are taken as T_q).  Only the first
  *               max_q_len rows of each sequence are computed and written:
  *               rows past them in a longer sequence keep what out held.
- * Other arguments as for decode.  This build implements D == 64,
+ * Other arguments as for decode.  This library implements D == 64,
  * block_size == 16 and Hq == 4 * Hkv.  Workgroups of 256 threads: one per
  * 32-row query tile, sequence and KV head; a sequence of at most 4 query
  * rows (a decoding sequence of a mixed batch, a few draft tokens) is one
@@ -506,7 +506,7 @@ PKV_API int paged_attention_prefill_causal(void *out, int32_t out_dtype, const v
  *               from each pool.
  * sink          device buffer of at least PKV_STREAM_SINK_BYTES; receives
  *               one folded word per lane (meaningless; it keeps the reads).
- * This build reads 2 KB chunks: D == 64 and block_size == 16.  The grid is
+ * This library reads 2 KB chunks: D == 64 and block_size == 16.  The grid is
  * 2048 wavefronts, each streaming an equal contiguous share of the chunks.
  */
 #define PKV_STREAM_SINK_BYTES (2048u * 64u * 4u)

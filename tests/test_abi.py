@@ -93,7 +93,7 @@ def test_decode_empty_batch_is_a_noop(lib):
 
 def test_decode_workspace_size(lib):
     """The query takes the contract's (B, Hq, D, max_context_len, partition_size):
-    the KV head count is Hq / 4 and the block size 16 in this build."""
+    the KV head count is Hq / 4 and the block size 16 in this library."""
     ws = pkv.paged_attention_decode_workspace_size
     assert ws(8, 32, 64, 2048, 0) == 0            # no split
     assert ws(8, 32, 64, 512, 512) == 0           # one partition covers everything
