@@ -353,11 +353,13 @@ def floor_record(us, nbytes, kernel_us):
             "decode_time_over_floor": round(kernel_us / us, 3)}
 
 
-def run_llama1b(torch, pkv, wl, steps, warmup, copies=8):
+def run_llama1b(torch, pkv, wl, steps, warmup, copies=16):
     """Llama-3.2-1B single-layer decode: batch 8, context uniform in
     [128, 2048], 4096-block pool, one new token per sequence appended then
-    attended.  `copies` pool pairs (128 MiB each, 1 GiB in all) are used in
-    turn so that no call finds the blocks in the last-level cache."""
+    attended.  `copies` pool pairs (128 MiB each) are used in turn; a call
+    touches 21 MB of them, so 16 copies (336 MB touched, 2 GiB allocated)
+    keep the 256 MB last-level cache from holding a call's blocks for its
+    next turn."""
     dev = "cuda"
     case = wl.device_decode_case("llama1b", dev, layers=copies)
     k_layers, v_layers = case.extra["k_layers"], case.extra["v_layers"]
@@ -441,7 +443,7 @@ def run_long_context(torch, pkv, wl, steps, warmup, copies=4):
     return res
 
 
-def run_mixed_batch(torch, pkv, wl, steps, warmup, copies=4):
+def run_mixed_batch(torch, pkv, wl, steps, warmup, copies=8):
     """One paged_attention_prefill_causal launch over a mixed continuous batch:
     60 sequences decoding one token each (context log-uniform in [16, 2048])
     and 4 prompt chunks of 256 tokens on 768 cached tokens (chunked prefill),
@@ -455,8 +457,9 @@ def run_mixed_batch(torch, pkv, wl, steps, warmup, copies=4):
     history = [int(L) - 1 for L in dec_lens] + [768] * 4
     p = wl.prefill_case(seed=21, prompts=prompts, history=history, num_blocks=8192)
     t, l, cu = p.block_tables.to(dev), p.context_lens.to(dev), p.cu_q_lens.to(dev)
-    # `copies` pool pairs (256 MiB each) used in turn: no call finds its blocks in
-    # the last-level cache
+    # `copies` pool pairs (256 MiB each) used in turn: a call touches about 62 MB,
+    # so 8 copies (500 MB touched) keep the last-level cache from holding a
+    # call's blocks for its next turn
     pools = []
     for _ in range(copies):
         kc, vc = p.k_cache.to(dev), p.v_cache.to(dev)

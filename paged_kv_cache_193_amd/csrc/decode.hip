@@ -121,7 +121,9 @@ __device__ __forceinline__ int eff_ctx(const Params& p, int b) {
 // `phys` was read earlier; `ub` receives the block's element offset for the
 // matching V loads (issue_v).  Returns the number of valid tokens in the
 // block (0 when `phys` is not a valid block id: then block 0 is read and
-// ignored).
+// ignored).  K and V are read once per call and never again by it, so their
+// loads carry the non-temporal hint: the streamed bytes do not displace the
+// plan, the block tables and the split records from the caches.
 __device__ __forceinline__ int issue_k(BlockRegs& r, const Params& p, int phys, int g, int j,
                                        int ctx, int lane_off, int64_t& ub) {
   int nv = ctx - j * kBS;
@@ -132,8 +134,8 @@ __device__ __forceinline__ int issue_k(BlockRegs& r, const Params& p, int phys, 
   }
   ub = ((int64_t)phys * p.Hkv + g) * (kBS * kD);
   const uint16_t* kp = p.k_cache + ub + lane_off;
-  r.ka = *reinterpret_cast<const u32x4*>(kp);
-  r.kb = *reinterpret_cast<const u32x4*>(kp + 8 * kD);
+  r.ka = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp));
+  r.kb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 8 * kD));
   return nv;
 }
 
@@ -141,8 +143,8 @@ __device__ __forceinline__ int issue_k(BlockRegs& r, const Params& p, int phys, 
 __device__ __forceinline__ void issue_v(BlockRegs& r, const Params& p, int64_t ub,
                                         int lane_off) {
   const uint16_t* vp = p.v_cache + ub + lane_off;
-  r.va = *reinterpret_cast<const u32x4*>(vp);
-  r.vb = *reinterpret_cast<const u32x4*>(vp + 8 * kD);
+  r.va = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp));
+  r.vb = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + 8 * kD));
 }
 
 // All four loads of a block at once (first group of a segment).

@@ -13,7 +13,7 @@
 // register.  The grid is the decode's automatic-split grid (2048 wavefronts);
 // each wavefront streams an equal contiguous share of the (block, head)
 // chunks, two chunks in flight, with 16-byte loads that cover whole
-// 128-byte rows.
+// 128-byte rows and carry the non-temporal hint, as the decode's do.
 #include "device_common.h"
 #include "launch.h"
 
@@ -43,22 +43,22 @@ stream_blocks_kernel(const uint16_t* __restrict__ k_cache, const uint16_t* __res
   int64_t c = c0;
   for (; c + 1 < c1; c += 2) {
     const int64_t a = chunk_base(c), b = chunk_base(c + 1);
-    const u32x4 k0 = *reinterpret_cast<const u32x4*>(k_cache + a);
-    const u32x4 k1 = *reinterpret_cast<const u32x4*>(k_cache + a + 8);
-    const u32x4 v0 = *reinterpret_cast<const u32x4*>(v_cache + a);
-    const u32x4 v1 = *reinterpret_cast<const u32x4*>(v_cache + a + 8);
-    const u32x4 k2 = *reinterpret_cast<const u32x4*>(k_cache + b);
-    const u32x4 k3 = *reinterpret_cast<const u32x4*>(k_cache + b + 8);
-    const u32x4 v2 = *reinterpret_cast<const u32x4*>(v_cache + b);
-    const u32x4 v3 = *reinterpret_cast<const u32x4*>(v_cache + b + 8);
+    const u32x4 k0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_cache + a));
+    const u32x4 k1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_cache + a + 8));
+    const u32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_cache + a));
+    const u32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_cache + a + 8));
+    const u32x4 k2 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_cache + b));
+    const u32x4 k3 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_cache + b + 8));
+    const u32x4 v2 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_cache + b));
+    const u32x4 v3 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_cache + b + 8));
     acc ^= k0 ^ k1 ^ v0 ^ v1 ^ k2 ^ k3 ^ v2 ^ v3;
   }
   if (c < c1) {
     const int64_t a = chunk_base(c);
-    acc ^= *reinterpret_cast<const u32x4*>(k_cache + a) ^
-           *reinterpret_cast<const u32x4*>(k_cache + a + 8) ^
-           *reinterpret_cast<const u32x4*>(v_cache + a) ^
-           *reinterpret_cast<const u32x4*>(v_cache + a + 8);
+    acc ^= __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_cache + a)) ^
+           __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k_cache + a + 8)) ^
+           __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_cache + a)) ^
+           __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v_cache + a + 8));
   }
   // one word per lane, so the loads cannot be dropped
   sink[w * 64 + lane] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
