@@ -131,23 +131,52 @@ hipError_t launch_kv_append(const KvAppendArgs& a, hipStream_t stream) {
 // owns elements [8c, 8c + 8) and [32 + 8c, 32 + 8c + 8) of its row, i.e. both
 // halves of 8 rotation pairs: two 16-byte loads, two 16-byte stores, and the
 // matching 32 bytes of cos and of sin.  A token's rows are consecutive, so
-// every wavefront reads and writes whole 128-byte rows.
+// every wavefront reads and writes whole 128-byte rows.  With at most 64
+// sequences a wavefront finds each token's sequence, its first new token and
+// its context length from one read of cu_new_lens and context_lens (a lane
+// per sequence) instead of a binary search of dependent reads: the kernel is
+// a short chain of round trips per thread, and each one removed shows.
 __global__ void __launch_bounds__(256)
 kv_append_rope_kernel(RopeAppendArgs a) {
   constexpr int kHalf = 32;  // D / 2, D == 64
   const int rows = a.Hq + 2 * a.Hkv;
-  const int64_t per_token = (int64_t)rows * 4;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)a.T_new * per_token) return;
+  // the grid holds fewer than 2^32 threads, so 32-bit indices suffice
+  const uint32_t per_token = (uint32_t)rows * 4u;
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
   const int t = (int)(gid / per_token);
-  const int rem = (int)(gid - (int64_t)t * per_token);
+  const int rem = (int)(gid - (uint32_t)t * per_token);
   const int r = rem >> 2, c = rem & 3;
+  // Up to 64 sequences: lane j holds cu_new_lens[j + 1] and context_lens[j],
+  // read in one round before any lane leaves, so that readlane and
+  // ds_bpermute see defined values.  The token's sequence is the number of
+  // sequences ending at or before t (cu_new_lens is non-decreasing), i.e.
+  // the largest b with cu_new_lens[b] <= t.
+  const bool few = a.cu_new_lens != nullptr && a.B <= 64;
+  int fb = 0, ffirst = 0, fend = 0, fctx = 0;
+  if (few) {
+    const int lane = threadIdx.x & 63;
+    const int ends = lane < a.B ? a.cu_new_lens[lane + 1] : 0x7FFFFFFF;
+    const int ctxs = lane < a.B ? a.context_lens[lane] : 0;
+    const int cu0 = a.cu_new_lens[0];
+    for (int j = 0; j < a.B; ++j) fb += __builtin_amdgcn_readlane(ends, j) <= t ? 1 : 0;
+    const int src = (fb & 63) * 4;  // fb == B only past the last token
+    fend = __builtin_amdgcn_ds_bpermute(src, ends);
+    fctx = __builtin_amdgcn_ds_bpermute(src, ctxs);
+    const int prev = __builtin_amdgcn_ds_bpermute(((fb - 1) & 63) * 4, ends);
+    ffirst = fb == 0 ? cu0 : prev;
+  }
+  if (gid >= (uint32_t)a.T_new * per_token) return;
 
-  int b, first, n;
+  int b, first, n, ctx_b = 0;
   if (a.cu_new_lens == nullptr) {
     b = t;
     first = t;
     n = 1;
+  } else if (few) {
+    b = fb;
+    first = ffirst;
+    n = fend - first;
+    ctx_b = fctx;
   } else {
     int lo = 0, hi = a.B;  // invariant: cu[lo] <= t < cu[hi]
     while (hi - lo > 1) {
@@ -158,7 +187,7 @@ kv_append_rope_kernel(RopeAppendArgs a) {
     first = a.cu_new_lens[b];
     n = a.cu_new_lens[b + 1] - first;
   }
-  const int pos = a.context_lens[b] - n + (t - first);
+  const int pos = (few ? ctx_b : a.context_lens[b]) - n + (t - first);
   if (pos < 0 || pos >= a.max_position) return;  // no angle for it: leave the token alone
 
   const bool is_q = r < a.Hq;
