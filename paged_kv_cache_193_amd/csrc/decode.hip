@@ -104,13 +104,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t records_ml(const Params& p) {
   return __builtin_amdgcn_make_buffer_rsrc(p.ws_ml, (short)0, p.n_records * 8 * 4, kRsrcWord3);
 }
 
-// Where the split records of one stream live: piece k of the stream is
-// record base + k * stride (+ first_extra for k == 0).
-struct RecordList {
-  int64_t base;
-  int stride, first_extra, pieces;
-};
-
 __device__ __forceinline__ int eff_ctx(const Params& p, int b) {
   int c = p.context_lens[b];
   c = c < 0 ? 0 : c;
@@ -219,7 +212,7 @@ __device__ __forceinline__ void block_pv(LaneState& st, const BlockRegs& r, floa
 // final rows out[b][4g..4g+3][:] or a split record.  red: this wave's 8 KB.
 __device__ __forceinline__ void finish_segment(const LaneState& st, const Params& p, int b,
                                                int g, bool complete, int record,
-                                               const RecordList& rl, float* red, int lane) {
+                                               float* red, int lane) {
   const int grp = lane >> 3, i = lane & 7;
   const bool quad1 = (i & 4) != 0;
   const int c = quad1 ? ((i & 3) ^ 3) : (i & 3);
@@ -304,7 +297,7 @@ __device__ __forceinline__ void drain_stores() {
 // Add one finished piece to stream (b, g)'s count (agent-scope atomic, issued
 // by lane 0; the piece's record stores must have completed: drain_stores())
 // and return the count before the addition, in every lane.  The wavefront
-// whose addition completes the count merges the pieces (merge_streams).
+// whose addition completes the count merges the pieces (merge_stream).
 __device__ __forceinline__ uint32_t count_piece(const Params& p, int b, int g, int lane) {
   uint32_t before = 0;
   if (lane == 0)
@@ -313,12 +306,6 @@ __device__ __forceinline__ uint32_t count_piece(const Params& p, int b, int g, i
                                     __HIP_MEMORY_SCOPE_AGENT);
   return __builtin_amdgcn_readfirstlane(before);
 }
-
-// A stream whose pieces this wave merges.
-struct MergeJob {
-  int b, g;
-  RecordList rl;
-};
 
 // Largest value / sum over the 64 lanes, returned wave-uniform: rotations
 // inside each row of 16 (DPP), then the four row results by readlane.
@@ -345,45 +332,39 @@ __device__ __forceinline__ float wave_sum_u(float v) {
           __builtin_bit_cast(float, __builtin_amdgcn_readlane(iv, 48)));
 }
 
-// Merge the pieces of N (1 or 2) streams by log-sum-exp,
+// Merge the P pieces of stream (b, g), whose records are base .. base + P - 1,
+// by log-sum-exp,
 //   out_h = sum_k w_k,h o_k,h / sum_k w_k,h,   w_k,h = l_k,h 2^(m_k,h - M_h),
-// write their rows and reset their counters.  Every read goes out before any
-// result is needed: the (m, l) of up to 64 pieces per stream (piece k in lane
-// k) and the o rows of the first kB pieces per stream, so merging two streams
-// of few pieces costs one round trip.  M_h and the sums are wave reductions;
-// the weights reach the lanes that accumulate head h through this wave's LDS
-// area `red` (head-major, 4 pieces per read).
-template <int N>
-__device__ __forceinline__ void merge_streams(const Params& p, const MergeJob (&job)[N],
-                                              float* red, int lane) {
+// write its rows and reset its counter.  Every read goes out before any
+// result is needed: the (m, l) of up to 64 pieces (piece k in lane k) and the
+// o rows of the first kB pieces, so merging a stream of up to kB pieces costs
+// one round trip.  M_h and the sums are wave reductions; the weights reach
+// the lanes that accumulate head h through this wave's LDS area `red`
+// (head-major, 4 pieces per read).
+__device__ __forceinline__ void merge_stream(const Params& p, int b, int g, int base, int P,
+                                             float* red, int lane) {
   const int h = lane >> 4;
   const int d4 = (lane & 15) * 4;
   const __amdgpu_buffer_rsrc_t rso = records_o(p);
   const __amdgpu_buffer_rsrc_t rsml = records_ml(p);
-  constexpr int kB = PKV_MERGE_BATCH / N;  // o rows per stream per round trip
-  static_assert(kB % 4 == 0, "o rows are weighted 4 pieces per LDS read");
+  constexpr int kB = PKV_MERGE_BATCH;  // o rows per round trip
+  static_assert(kB % 4 == 0 && 64 % kB == 0, "o rows are weighted 4 pieces per LDS read");
   const int o_off = (h * kD + d4) * 4;
-  auto rec = [&](int n, int k) -> int {
-    const RecordList& rl = job[n].rl;
-    return (int)(rl.base + (int64_t)k * rl.stride + (k == 0 ? rl.first_extra : 0));
+  // piece k, clamped to the last (reads past the stream repeat it, weight 0)
+  auto rec = [&](int k) -> int { return base + (k < P ? k : P - 1); };
+  auto load_o = [&](int k) -> f32x4 {
+    return __builtin_amdgcn_raw_buffer_load_b128(rso, rec(k) * (kRecordFloats * 4) + o_off, 0,
+                                                 kSc1);
   };
-  auto load_o = [&](int n, int k) -> f32x4 {
-    const int P = job[n].rl.pieces;
-    return __builtin_amdgcn_raw_buffer_load_b128(
-        rso, rec(n, k < P ? k : P - 1) * (kRecordFloats * 4) + o_off, 0, kSc1);
-  };
-  // (m, l) of piece c0 + lane of stream n: (m0 l0 m1 l1), (m2 l2 m3 l3)
-  auto load_ml = [&](int n, int c0, f32x4& lo, f32x4& hi) {
-    const int P = job[n].rl.pieces;
-    const int k = c0 + lane;
-    const int r = rec(n, k < P ? k : P - 1);
+  // (m, l) of piece c0 + lane: (m0 l0 m1 l1), (m2 l2 m3 l3)
+  auto load_ml = [&](int c0, f32x4& lo, f32x4& hi) {
+    const int r = rec(c0 + lane);
     lo = __builtin_amdgcn_raw_buffer_load_b128(rsml, r * 32, 0, kSc1);
     hi = __builtin_amdgcn_raw_buffer_load_b128(rsml, r * 32 + 16, 0, kSc1);
   };
   // this lane's piece: m and l per head, l = 0 past the stream's pieces
-  auto unpack = [&](int n, int c0, const f32x4& lo, const f32x4& hi, float (&m)[4],
-                    float (&l)[4]) {
-    const bool in = c0 + lane < job[n].rl.pieces;
+  auto unpack = [&](int c0, const f32x4& lo, const f32x4& hi, float (&m)[4], float (&l)[4]) {
+    const bool in = c0 + lane < P;
     m[0] = lo[0]; m[1] = lo[2]; m[2] = hi[0]; m[3] = hi[2];
     l[0] = in ? lo[1] : 0.f; l[1] = in ? lo[3] : 0.f;
     l[2] = in ? hi[1] : 0.f; l[3] = in ? hi[3] : 0.f;
@@ -394,79 +375,70 @@ __device__ __forceinline__ void merge_streams(const Params& p, const MergeJob (&
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   };
 
-  f32x4 ob[N][kB];
-  f32x4 ml_lo[N], ml_hi[N];
+  f32x4 ob[kB];
+  f32x4 ml_lo, ml_hi;
+  load_ml(0, ml_lo, ml_hi);
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    load_ml(n, 0, ml_lo[n], ml_hi[n]);
-#pragma unroll
-    for (int u = 0; u < kB; ++u) ob[n][u] = load_o(n, u);
-  }
+  for (int u = 0; u < kB; ++u) ob[u] = load_o(u);
 
+  float m[4], l[4], M[4];
+  unpack(0, ml_lo, ml_hi, m, l);
+  // maxima over all pieces (l > 0 only)
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    const int P = job[n].rl.pieces;
-    float m[4], l[4], M[4];
-    unpack(n, 0, ml_lo[n], ml_hi[n], m, l);
-    // maxima over all pieces (l > 0 only)
+  for (int hh = 0; hh < 4; ++hh) M[hh] = wave_max_u(l[hh] > 0.f ? m[hh] : -INFINITY);
+  for (int c0 = 64; c0 < P; c0 += 64) {
+    f32x4 lo, hi;
+    float mc[4], lc[4];
+    load_ml(c0, lo, hi);
+    unpack(c0, lo, hi, mc, lc);
 #pragma unroll
-    for (int hh = 0; hh < 4; ++hh) M[hh] = wave_max_u(l[hh] > 0.f ? m[hh] : -INFINITY);
-    for (int c0 = 64; c0 < P; c0 += 64) {
-      f32x4 lo, hi;
-      float mc[4], lc[4];
-      load_ml(n, c0, lo, hi);
-      unpack(n, c0, lo, hi, mc, lc);
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh)
-        M[hh] = fmaxf(M[hh], wave_max_u(lc[hh] > 0.f ? mc[hh] : -INFINITY));
-    }
-    float* wr = red + n * 256;  // weights [head][64 pieces]
-    float den_h = 0.f;
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = 0; c0 < P; c0 += 64) {
-      if (c0 > 0) {
-        f32x4 lo, hi;
-        load_ml(n, c0, lo, hi);
-        unpack(n, c0, lo, hi, m, l);
-      }
-      lds_sync();  // earlier readers of wr are done
-#pragma unroll
-      for (int hh = 0; hh < 4; ++hh) {
-        const float w = l[hh] > 0.f ? l[hh] * __builtin_amdgcn_exp2f(m[hh] - M[hh]) : 0.f;
-        wr[hh * 64 + lane] = w;
-        const float t = wave_sum_u(w);
-        den_h = hh == h ? den_h + t : den_h;
-      }
-      lds_sync();
-      const int cn = P - c0 < 64 ? P - c0 : 64;
-      for (int k0 = 0; k0 < cn; k0 += kB) {
-        if (c0 + k0 > 0) {
-#pragma unroll
-          for (int u = 0; u < kB; ++u) ob[n][u] = load_o(n, c0 + k0 + u);
-        }
-#pragma unroll
-        for (int u = 0; u < kB; u += 4) {
-          // weights of pieces k0+u .. k0+u+3 (0 past the stream's pieces)
-          const f32x4 w4 = *reinterpret_cast<const f32x4*>(wr + h * 64 + (k0 + u < 60 ? k0 + u : 60));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) num += w4[e] * ob[n][u + e];
-        }
-      }
-    }
-    const float inv = den_h > 0.f ? 1.0f / den_h : 0.f;
-    const float4 res = make_float4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
-    const int64_t row = ((int64_t)job[n].b * p.Hq + 4 * job[n].g + h) * kD + d4;
-    if (p.out_f32) {
-      *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row) = res;
-    } else {
-      u32x2 pk = {pack_bf16(res.x, res.y), pack_bf16(res.z, res.w)};
-      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + row) = pk;
-    }
-    if (lane == 0)
-      __hip_atomic_store(p.ws_count + ((int64_t)job[n].b * p.Hkv + job[n].g) * kCounterStride, 0u,
-                         __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+    for (int hh = 0; hh < 4; ++hh)
+      M[hh] = fmaxf(M[hh], wave_max_u(lc[hh] > 0.f ? mc[hh] : -INFINITY));
   }
+  float den_h = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < P; c0 += 64) {
+    if (c0 > 0) {
+      f32x4 lo, hi;
+      load_ml(c0, lo, hi);
+      unpack(c0, lo, hi, m, l);
+    }
+    lds_sync();  // earlier readers of red are done
+#pragma unroll
+    for (int hh = 0; hh < 4; ++hh) {
+      const float w = l[hh] > 0.f ? l[hh] * __builtin_amdgcn_exp2f(m[hh] - M[hh]) : 0.f;
+      red[hh * 64 + lane] = w;  // weights [head][64 pieces]
+      const float t = wave_sum_u(w);
+      den_h = hh == h ? den_h + t : den_h;
+    }
+    lds_sync();
+    const int cn = P - c0 < 64 ? P - c0 : 64;
+    for (int k0 = 0; k0 < cn; k0 += kB) {
+      if (c0 + k0 > 0) {
+#pragma unroll
+        for (int u = 0; u < kB; ++u) ob[u] = load_o(c0 + k0 + u);
+      }
+#pragma unroll
+      for (int u = 0; u < kB; u += 4) {
+        // weights of pieces k0+u .. k0+u+3 (0 past the stream's pieces)
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(red + h * 64 + k0 + u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) num += w4[e] * ob[u + e];
+      }
+    }
+  }
+  const float inv = den_h > 0.f ? 1.0f / den_h : 0.f;
+  const float4 res = make_float4(num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv);
+  const int64_t row = ((int64_t)b * p.Hq + 4 * g + h) * kD + d4;
+  if (p.out_f32) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.out) + row) = res;
+  } else {
+    u32x2 pk = {pack_bf16(res.x, res.y), pack_bf16(res.z, res.w)};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + row) = pk;
+  }
+  if (lane == 0)
+    __hip_atomic_store(p.ws_count + ((int64_t)b * p.Hkv + g) * kCounterStride, 0u,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void write_zero_rows(const Params& p, int b, int g, int lane) {
@@ -848,18 +820,12 @@ decode_units_kernel(Params p) {
   LaneState st;
   piece_run<false>(st, r, p, pc, false, lane);
   const bool complete = (j0 == 0 && j1 == nb);
-  RecordList rl;
-  rl.base = (int64_t)stream * parts;
-  rl.stride = 1;
-  rl.first_extra = 0;
-  rl.pieces = (nb + p.part_blocks - 1) / (p.part_blocks > 0 ? p.part_blocks : 1);
-  finish_segment(st, p, b, g, complete, unit, rl, red[wave], lane);
+  const int pieces = (nb + p.part_blocks - 1) / (p.part_blocks > 0 ? p.part_blocks : 1);
+  finish_segment(st, p, b, g, complete, unit, red[wave], lane);
   if (!complete) {
     drain_stores();
-    if (count_piece(p, b, g, lane) + 1 == (uint32_t)rl.pieces) {
-      const MergeJob job[1] = {{b, g, rl}};
-      merge_streams<1>(p, job, red[wave], lane);
-    }
+    if (count_piece(p, b, g, lane) + 1 == (uint32_t)pieces)
+      merge_stream(p, b, g, stream * parts, pieces, red[wave], lane);
   }
 }
 
@@ -1040,18 +1006,11 @@ decode_auto_kernel(Params p) {
   LaneState st;
   piece_run<kAppend>(st, r, p, pc, app, lane);
   const bool complete = pc.pieces == 1;
-  RecordList rl;
-  rl.base = pc.base;
-  rl.stride = 1;
-  rl.first_extra = 0;
-  rl.pieces = pc.pieces;
-  finish_segment(st, p, pc.b, pc.g, complete, pc.base + pc.k, rl, red[wave], lane);
+  finish_segment(st, p, pc.b, pc.g, complete, pc.base + pc.k, red[wave], lane);
   if (!complete) {
     drain_stores();
-    if (count_piece(p, pc.b, pc.g, lane) + 1 == (uint32_t)pc.pieces) {
-      const MergeJob job[1] = {{pc.b, pc.g, rl}};
-      merge_streams<1>(p, job, red[wave], lane);
-    }
+    if (count_piece(p, pc.b, pc.g, lane) + 1 == (uint32_t)pc.pieces)
+      merge_stream(p, pc.b, pc.g, pc.base, pc.pieces, red[wave], lane);
   }
 }
 
