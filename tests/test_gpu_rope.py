@@ -124,16 +124,19 @@ def test_ragged_new_tokens(with_q):
           f"ragged q={with_q}")
 
 
-@pytest.mark.parametrize("B", [64, 65, 130])
+@pytest.mark.parametrize("B", [1, 2, 64, 65, 130])
 def test_many_sequences(B):
-    """Batches at and past 64 sequences: up to 64 a wavefront finds each
-    token's sequence from one read of the lengths, beyond that by binary
-    search.  Sequences without new tokens, alone and in a run (equal
+    """Batch sizes on both sides of 64 sequences: up to 64 a wavefront finds
+    each token's sequence from one read of the lengths, beyond that by
+    binary search.  Sequences without new tokens, alone and in a run (equal
     consecutive cu_new_lens entries), must not capture any token."""
     g = np.random.default_rng(930 + B)
     new = g.integers(0, 6, B)
-    new[::7] = 0
-    new[B // 2:B // 2 + 5] = 0
+    if B > 8:
+        new[::7] = 0
+        new[B // 2:B // 2 + 5] = 0
+    else:
+        new = np.maximum(new, 1)
     lens = (new + g.integers(0, 60, B)).tolist()
     kc, vc, kn, vn, tables, lens_t, cu, q = ragged_case(93 + B, new.tolist(), lens,
                                                         num_blocks=1024, max_blocks=8)
